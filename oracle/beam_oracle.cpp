@@ -1,0 +1,273 @@
+// Beam sparse-MoE layer forward: plain CPU oracle.
+//
+// TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's CPU
+// baseline leg may load this library. It shares no code, header or table with
+// the GPU path; the two meet only through the seeded input generator.
+//
+// What it computes, in IEEE double, in the order the pages state it:
+//   * pre-MLP RMSNorm (sandwich norm) of the hidden states, rounded once to bf16
+//     [Transformers "Beam" model page, Overview: sandwich norms; FP32 numerics note;
+//      BeamConfig: rms_norm_eps] -- large-chunk workload only;
+//   * router logits z = x . Wr, sigmoid scores s, biased scores b = s + bias
+//     [Transformers "Beam" page, Overview: sparse MoE item and FP32 routing note;
+//      archdb "Beam-1.0-501B-A23B" fact sheet, MoE: gating function, load balancing];
+//   * group score = sum of the two largest biased scores in the group; keep the
+//     topk_group best groups; top_k experts by biased score inside them
+//     [archdb fact sheet, MoE: expert groups row; Transformers "Beam" page,
+//      BeamConfig: n_group, topk_group, num_experts_per_tok; news.hamidun.com
+//      article, section on where Beam saves and where it pays in memory];
+//   * weights = unbiased scores of the chosen experts renormalised to sum to 1,
+//     times routed_scaling_factor [archdb fact sheet, MoE: renormalisation and
+//     routed scaling rows; Transformers "Beam" page, BeamConfig: norm_topk_prob,
+//     routed_scaling_factor];
+//   * per chosen expert a SwiGLU MLP without biases, intermediate 2560
+//     [Transformers "Beam" page, BeamConfig: hidden_act, moe_intermediate_size;
+//      archdb fact sheet, FFN rows];
+//   * y = sum of the weighted expert outputs, no shared expert [archdb fact sheet,
+//     MoE: always-on experts = 0].
+//
+// Readings taken where the pages leave a step open:
+//   - the bias selects only: group scores and the top-k use b, the weights use s;
+//   - groups are contiguous blocks of E/n_group expert ids;
+//   - ties go to the lower group / expert index;
+//   - the SwiGLU output h is rounded to bf16 once before the down projection
+//     (the down projection is a bf16 GEMM); y is reported without rounding;
+//   - the RMSNorm output is rounded to bf16 once, x = bf16((h * r) * w).
+//
+// Layouts (row-major): x [T,d] bf16 bits, Wr [d,E] fp32, bias [E] fp32,
+// Wg[e], Wu[e] [I,d] bf16 bits (one row per intermediate channel), Wd[e] [d,I].
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <numeric>
+#include <thread>
+#include <vector>
+
+namespace {
+
+double bf16_value(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    std::memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+// Round a double to the nearest bfloat16 (8 significant bits), ties to even,
+// by scaling to an integer grid with exact power-of-two factors.
+uint16_t bf16_round(double v) {
+    if (std::isnan(v)) return 0x7fc0;
+    if (v == 0.0) return std::signbit(v) ? 0x8000 : 0x0000;
+    int ex;
+    std::frexp(v, &ex);                  // v = f * 2^ex, 0.5 <= |f| < 1
+    int q_exp = ex - 8;                  // spacing of bf16 values around v
+    if (q_exp < -133) q_exp = -133;      // subnormal spacing
+    double q = std::ldexp(v, -q_exp);    // exact
+    double r = std::nearbyint(q);        // round half to even (default mode)
+    double out = std::ldexp(r, q_exp);   // exact when representable
+    const double bf16_max = 3.38953138925153547590470800371487866880e38;
+    if (std::fabs(out) > bf16_max) out = std::copysign(INFINITY, v);
+    float f = (float)out;                // exact: out has <= 8 significant bits
+    uint32_t u;
+    std::memcpy(&u, &f, 4);
+    return (uint16_t)(u >> 16);
+}
+
+template <class F>
+void parallel_for(int64_t n, int nthreads, F f) {
+    if (nthreads <= 1 || n <= 1) {
+        for (int64_t i = 0; i < n; ++i) f(i);
+        return;
+    }
+    if (nthreads > n) nthreads = (int)n;
+    std::vector<std::thread> th;
+    for (int t = 0; t < nthreads; ++t)
+        th.emplace_back([=, &f]() {
+            for (int64_t i = t; i < n; i += nthreads) f(i);
+        });
+    for (auto& x : th) x.join();
+}
+
+double sigmoid(double z) { return 1.0 / (1.0 + std::exp(-z)); }
+
+struct Route {
+    std::vector<int32_t> idx;   // top_k expert ids, descending biased score
+    std::vector<double> w;      // routing weights aligned with idx
+    double gap;                 // smallest score gap at a selection boundary
+};
+
+// Routing of one token from its logits (double).
+Route route_token(const double* z, const float* bias, int E, int G, int KG, int K, double S, int norm) {
+    const int gsz = E / G;
+    std::vector<double> s(E), b(E);
+    for (int e = 0; e < E; ++e) {
+        s[e] = sigmoid(z[e]);
+        b[e] = s[e] + (double)bias[e];
+    }
+    // Group score: the two largest biased scores of the group, summed.
+    std::vector<double> gs(G);
+    for (int g = 0; g < G; ++g) {
+        std::vector<double> v(b.begin() + (int64_t)g * gsz, b.begin() + (int64_t)(g + 1) * gsz);
+        std::sort(v.begin(), v.end(), std::greater<double>());
+        gs[g] = v[0] + v[1];
+    }
+    // Keep the KG best groups (lower index first on equal scores).
+    std::vector<int> gord(G);
+    std::iota(gord.begin(), gord.end(), 0);
+    std::stable_sort(gord.begin(), gord.end(), [&](int a, int c) { return gs[a] > gs[c]; });
+    std::vector<char> kept(G, 0);
+    for (int i = 0; i < KG; ++i) kept[gord[i]] = 1;
+    // Candidates: experts of kept groups; the rest are excluded outright.
+    std::vector<int> cand;
+    for (int e = 0; e < E; ++e)
+        if (kept[e / gsz]) cand.push_back(e);
+    std::stable_sort(cand.begin(), cand.end(), [&](int a, int c) { return b[a] > b[c]; });
+    Route r;
+    r.idx.assign(cand.begin(), cand.begin() + K);
+    double sum = 0.0;
+    for (int j = 0; j < K; ++j) sum += s[r.idx[j]];
+    r.w.resize(K);
+    for (int j = 0; j < K; ++j) r.w[j] = norm ? S * s[r.idx[j]] / sum : S * s[r.idx[j]];
+    double gap = INFINITY;
+    if (KG < G) gap = std::min(gap, gs[gord[KG - 1]] - gs[gord[KG]]);
+    if (K < (int)cand.size()) gap = std::min(gap, b[cand[K - 1]] - b[cand[K]]);
+    r.gap = gap;
+    return r;
+}
+
+void logits_token(const uint16_t* xrow, const float* Wr, int d, int E, double* z) {
+    for (int e = 0; e < E; ++e) z[e] = 0.0;
+    for (int j = 0; j < d; ++j) {
+        double xv = bf16_value(xrow[j]);
+        const float* wrow = Wr + (int64_t)j * E;
+        for (int e = 0; e < E; ++e) z[e] += xv * (double)wrow[e];
+    }
+}
+
+// One expert applied to one token: o = Wd . bf16(silu(Wg . x) * (Wu . x)).
+void expert_token(const uint16_t* xrow, const uint16_t* wg, const uint16_t* wu, const uint16_t* wd,
+                  int d, int I, double* o) {
+    std::vector<double> xv(d), h(I);
+    for (int j = 0; j < d; ++j) xv[j] = bf16_value(xrow[j]);
+    for (int n = 0; n < I; ++n) {
+        const uint16_t* gr = wg + (int64_t)n * d;
+        const uint16_t* ur = wu + (int64_t)n * d;
+        double g = 0.0, u = 0.0;
+        for (int j = 0; j < d; ++j) {
+            g += xv[j] * bf16_value(gr[j]);
+            u += xv[j] * bf16_value(ur[j]);
+        }
+        double a = g / (1.0 + std::exp(-g)) * u;   // silu(g) * u
+        h[n] = bf16_value(bf16_round(a));
+    }
+    for (int c = 0; c < d; ++c) {
+        const uint16_t* dr = wd + (int64_t)c * I;
+        double acc = 0.0;
+        for (int n = 0; n < I; ++n) acc += h[n] * bf16_value(dr[n]);
+        o[c] = acc;
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+// The bf16 rounding the oracle applies to h and to the normed x, exposed so it can be pinned.
+void oracle_bf16_round(const double* v, int64_t n, uint16_t* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = bf16_round(v[i]);
+}
+
+// x[t,j] = bf16((h[t,j] * r_t) * w[j]), r_t = 1 / sqrt(mean_j h[t,j]^2 + eps).
+void oracle_rmsnorm(const uint16_t* h, const uint16_t* w, int64_t T, int32_t d, double eps,
+                    uint16_t* x_out, int32_t nthreads) {
+    parallel_for(T, nthreads, [&](int64_t t) {
+        const uint16_t* hr = h + t * d;
+        double ss = 0.0;
+        for (int j = 0; j < d; ++j) {
+            double v = bf16_value(hr[j]);
+            ss += v * v;
+        }
+        double r = 1.0 / std::sqrt(ss / d + eps);
+        for (int j = 0; j < d; ++j) x_out[t * d + j] = bf16_round(bf16_value(hr[j]) * r * bf16_value(w[j]));
+    });
+}
+
+// Raw router logits z [T,E] (double).
+void oracle_logits(const uint16_t* x, const float* Wr, int64_t T, int32_t d, int32_t E, double* z_out,
+                   int32_t nthreads) {
+    parallel_for(T, nthreads, [&](int64_t t) { logits_token(x + t * d, Wr, d, E, z_out + t * E); });
+}
+
+// Routing of T tokens: idx [T,K] (descending biased score), w [T,K], gap [T]; z_out [T,E] optional.
+void oracle_route(const uint16_t* x, const float* Wr, const float* bias, int64_t T, int32_t d, int32_t E,
+                  int32_t G, int32_t KG, int32_t K, double S, int32_t norm, int32_t* idx_out, double* w_out,
+                  double* gap_out, double* z_out, int32_t nthreads) {
+    parallel_for(T, nthreads, [&](int64_t t) {
+        std::vector<double> zl(E);
+        double* z = z_out ? z_out + t * E : zl.data();
+        logits_token(x + t * d, Wr, d, E, z);
+        Route r = route_token(z, bias, E, G, KG, K, S, norm);
+        for (int j = 0; j < K; ++j) {
+            idx_out[t * K + j] = r.idx[j];
+            w_out[t * K + j] = r.w[j];
+        }
+        gap_out[t] = r.gap;
+    });
+}
+
+// Routing weights for a given selection idx [T,K] (used when a token's selection is excused).
+void oracle_weights_for(const double* z, int64_t T, int32_t E, int32_t K, const int32_t* idx, double S,
+                        int32_t norm, double* w_out) {
+    for (int64_t t = 0; t < T; ++t) {
+        double sum = 0.0;
+        for (int j = 0; j < K; ++j) sum += sigmoid(z[t * E + idx[t * K + j]]);
+        for (int j = 0; j < K; ++j) {
+            double s = sigmoid(z[t * E + idx[t * K + j]]);
+            w_out[t * K + j] = norm ? S * s / sum : S * s;
+        }
+    }
+}
+
+// Token -> expert dispatch: pairs p = t*K + j ordered by expert id, stably.
+// offsets [E+1], sorted_pairs [P], pair_rank [P] (position of pair p in sorted order).
+void oracle_dispatch(const int32_t* idx, int64_t P, int32_t E, int32_t* offsets, int32_t* sorted_pairs,
+                     int32_t* pair_rank) {
+    std::vector<int32_t> order(P);
+    std::iota(order.begin(), order.end(), 0);
+    std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t c) { return idx[a] < idx[c]; });
+    for (int e = 0; e <= E; ++e) offsets[e] = 0;
+    for (int64_t p = 0; p < P; ++p) offsets[idx[p] + 1] += 1;
+    for (int e = 0; e < E; ++e) offsets[e + 1] += offsets[e];
+    for (int64_t i = 0; i < P; ++i) {
+        sorted_pairs[i] = order[i];
+        pair_rank[order[i]] = (int32_t)i;
+    }
+}
+
+// One expert on n token rows: o [n,d] (double), with the bf16 rounding of h.
+void oracle_expert(const uint16_t* x_rows, int64_t n, const uint16_t* wg, const uint16_t* wu, const uint16_t* wd,
+                   int32_t d, int32_t I, double* o_out, int32_t nthreads) {
+    parallel_for(n, nthreads, [&](int64_t i) { expert_token(x_rows + i * d, wg, wu, wd, d, I, o_out + i * d); });
+}
+
+// Layer output for n token rows given their routing: y[i] = sum_j w[i,j] * expert_{idx[i,j]}(x[i]).
+// Expert weights are passed per expert id (arrays of E pointers; unused entries may be NULL).
+void oracle_moe_rows(const uint16_t* x_rows, int64_t n, const int32_t* idx, const double* w, int32_t K,
+                     const uint16_t* const* wg, const uint16_t* const* wu, const uint16_t* const* wd,
+                     int32_t d, int32_t I, double* y_out, int32_t nthreads) {
+    int64_t work = n * K;
+    std::vector<double> o((size_t)work * d);
+    parallel_for(work, nthreads, [&](int64_t q) {
+        int64_t i = q / K;
+        int e = idx[q];
+        expert_token(x_rows + i * d, wg[e], wu[e], wd[e], d, I, o.data() + q * d);
+    });
+    for (int64_t i = 0; i < n; ++i)
+        for (int c = 0; c < d; ++c) {
+            double acc = 0.0;
+            for (int j = 0; j < K; ++j) acc += w[i * K + j] * o[(i * K + j) * d + c];
+            y_out[i * d + c] = acc;
+        }
+}
+
+}  // extern "C"

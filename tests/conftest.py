@@ -1,0 +1,25 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
+    config.addinivalue_line("markers", "slow: CPU test that takes more than a few seconds")
+
+
+def _ensure_host_libs():
+    import synth
+    import oracle
+    if not os.path.exists(synth.HOST_LIB):
+        synth.build()
+    if not os.path.exists(oracle.LIB):
+        oracle.build()
+
+
+_ensure_host_libs()

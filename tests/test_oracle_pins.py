@@ -1,0 +1,317 @@
+"""Pins of the CPU oracle against things other than itself: published numbers,
+closed forms, brute force, invariants and special cases that reduce to library
+routines (numpy / torch float64). Each test names what a plausible mistake in
+the oracle would break."""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from synth import recipes
+from tests import _ref
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _tiny_inputs(w, seed_shift=0):
+    ws = recipes.Workload(**{**w.__dict__, "seed_base": w.seed_base + seed_shift})
+    x = synth.hidden(ws)
+    Wr = synth.router_weight(ws)
+    b = synth.bias(ws)
+    return ws, x, Wr, b
+
+
+# --- published numbers -------------------------------------------------------------------
+
+def test_golden_shape_facts():
+    """Constants of the workloads against the numbers printed on the pages."""
+    g = json.load(open(os.path.join(GOLDEN, "beam_shape_facts.json")))
+    w = recipes.WORKLOADS[2]
+    assert w.d == g["hidden_size"]["value"]
+    assert w.I == g["moe_intermediate_size"]["value"]
+    assert w.E == g["num_experts"]["value"]
+    assert w.top_k == g["num_experts_per_tok"]["value"]
+    assert w.n_group == g["n_group"]["value"]
+    assert w.topk_group == g["topk_group"]["value"]
+    assert w.E // w.n_group == g["experts_per_group"]["value"]
+    assert w.scale == g["routed_scaling_factor"]["value"]
+    assert w.eps == g["rms_norm_eps"]["value"]
+    per_expert = 3 * w.d * w.I                        # gate, up, down; no biases
+    assert per_expert == 39_321_600
+    assert round(per_expert / 1e6) == g["params_per_expert_approx_millions"]["value"]
+    share = g["moe_layers"]["value"] * w.E * per_expert / (g["total_params_billions"]["value"] * 1e9)
+    assert round(100 * share, 1) == g["expert_weight_share_percent"]["value"]
+    emb = 2 * g["vocab_size"]["value"] * w.d          # untied embedding + head
+    assert round(emb / 1e9, 3) == g["embedding_plus_head_billions"]["value"]
+    assert w.E // w.top_k == g["experts_over_top_k"]["value"]
+    assert w.I / w.d == g["expert_dim_over_d_model"]["value"]
+    ratio = g["active_params_billions"]["value"] / g["total_params_billions"]["value"]
+    assert round(ratio, 7) == g["active_over_total"]["value"]
+
+
+# --- bf16 rounding -------------------------------------------------------------------------
+
+def test_bf16_round_cases_and_random():
+    one = 1.0
+    cases = {
+        one: 0x3F80,
+        one + 2 ** -8: 0x3F80,             # halfway, ties to even (down)
+        one + 3 * 2 ** -8: 0x3F82,         # halfway, ties to even (up)
+        one + 2 ** -8 + 2 ** -30: 0x3F81,  # just above halfway
+        -2.0: 0xC000,
+        0.0: 0x0000,
+        2.0 ** -133: 0x0001,               # smallest subnormal
+        3.0e38: 0x7F62,
+    }
+    got = oracle.bf16_round(np.array(list(cases.keys())))
+    assert [int(v) for v in got] == list(cases.values())
+    rng = np.random.default_rng(0)
+    v = rng.standard_normal(200_000) * np.exp(rng.uniform(-30, 30, 200_000))
+    assert np.array_equal(oracle.bf16_round(v), _ref.f64_to_bf16_bits_rne(v))
+
+
+# --- router -------------------------------------------------------------------------------
+
+def test_logits_onehot_and_matmul():
+    w = recipes.WORKLOADS[0]
+    _, x, Wr, _ = _tiny_inputs(w)
+    onehot = np.zeros((w.d, w.d), dtype=np.uint16)
+    onehot[np.arange(w.d), np.arange(w.d)] = 0x3F80   # bf16 1.0
+    z = oracle.logits(onehot, Wr)
+    assert np.array_equal(z, Wr.astype(np.float64))  # one-hot x picks a row of Wr exactly
+    z = oracle.logits(x, Wr)
+    ref = _ref.bf16_bits_to_f64(x) @ Wr.astype(np.float64)
+    np.testing.assert_allclose(z, ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed_shift", [0, 1, 2])
+def test_route_matches_brute_force_tiny(seed_shift):
+    """Exhaustive enumeration of group pairs, group subsets and expert subsets."""
+    w = recipes.WORKLOADS[0]
+    ws, x, Wr, b = _tiny_inputs(w, seed_shift)
+    idx, wt, gap, z = oracle.route(x, Wr, b, w.n_group, w.topk_group, w.top_k, w.scale, want_logits=True)
+    zr = _ref.bf16_bits_to_f64(x) @ Wr.astype(np.float64)
+    checked = 0
+    for t in range(w.T):
+        if gap[t] < 1e-9:
+            continue
+        sel, wref = _ref.brute_route_token(zr[t], b, w.n_group, w.topk_group, w.top_k, w.scale)
+        assert sorted(idx[t].tolist()) == sel, t
+        for j in range(w.top_k):
+            assert abs(wt[t, j] - wref[int(idx[t, j])]) < 1e-12
+        checked += 1
+    assert checked >= w.T - 2
+
+
+def test_route_random_small_shapes_brute_force():
+    rng = np.random.default_rng(1)
+    for (E, G, KG, K) in [(8, 2, 1, 2), (12, 3, 2, 3), (16, 4, 3, 5), (16, 8, 3, 4), (20, 5, 5, 6)]:
+        d = 64
+        x = _ref.f64_to_bf16_bits_rne(rng.standard_normal((40, d)))
+        Wr = (rng.standard_normal((d, E)) / 8).astype(np.float32)
+        bias = rng.uniform(-0.3, 0.3, E).astype(np.float32)
+        idx, wt, gap = oracle.route(x, Wr, bias, G, KG, K, 2.5)
+        zr = _ref.bf16_bits_to_f64(x) @ Wr.astype(np.float64)
+        for t in range(40):
+            if gap[t] < 1e-9:
+                continue
+            sel, _ = _ref.brute_route_token(zr[t], bias, G, KG, K, 2.5)
+            assert sorted(idx[t].tolist()) == sel
+
+
+def test_route_full_shape_group_stage_and_certificate():
+    """Beam shape: group scores by all 496 pairs per group, kept groups by all 70
+    subsets, chosen experts certified by min(chosen b) > max(other candidate b)."""
+    w = recipes.WORKLOADS[2].with_T(48)
+    x = synth.hidden(w)
+    Wr = synth.router_weight(w)
+    b = synth.bias(w)
+    idx, wt, gap, z = oracle.route(x, Wr, b, w.n_group, w.topk_group, w.top_k, w.scale, want_logits=True)
+    s = _ref.sigmoid(z)
+    bb = s + b.astype(np.float64)
+    gsz = w.E // w.n_group
+    for t in range(w.T):
+        gs = [max(bb[t, i] + bb[t, j] for i, j in itertools.combinations(range(g * gsz, (g + 1) * gsz), 2))
+              for g in range(w.n_group)]
+        kept = max(itertools.combinations(range(w.n_group), w.topk_group), key=lambda c: sum(gs[g] for g in c))
+        groups = {int(e) // gsz for e in idx[t]}
+        assert groups <= set(kept)
+        cand = [e for g in kept for e in range(g * gsz, (g + 1) * gsz)]
+        others = [e for e in cand if e not in set(idx[t].tolist())]
+        assert bb[t, idx[t]].min() > bb[t, others].max()
+        assert np.all(np.diff(bb[t, idx[t]]) < 0)          # descending biased score
+        assert abs(wt[t].sum() - w.scale) < 1e-12
+        np.testing.assert_allclose(wt[t] / wt[t].sum(), s[t, idx[t]] / s[t, idx[t]].sum(), rtol=1e-13)
+
+
+def test_route_invariants():
+    w = recipes.WORKLOADS[0]
+    _, x, Wr, b = _tiny_inputs(w)
+    G, KG, K, S = w.n_group, w.topk_group, w.top_k, w.scale
+    idx, wt, gap, z = oracle.route(x, Wr, b, G, KG, K, S, want_logits=True)
+    ok = gap > 1e-9
+    # weights sum to the routed scaling factor; at most KG groups per token
+    np.testing.assert_allclose(wt.sum(1), S, rtol=0, atol=1e-12)
+    assert max(len({e // (w.E // G) for e in row}) for row in idx) <= KG
+    # a constant bias shift selects the same experts with the same weights (bias only selects)
+    idx2, wt2, _ = oracle.route(x, Wr, b + np.float32(0.25), G, KG, K, S)
+    assert np.array_equal(idx[ok], idx2[ok])
+    assert np.array_equal(wt[ok], wt2[ok])
+    # weights are proportional to the unbiased sigmoid scores of the chosen experts
+    s = _ref.sigmoid(z)
+    for t in np.nonzero(ok)[0]:
+        np.testing.assert_allclose(wt[t], S * s[t, idx[t]] / s[t, idx[t]].sum(), rtol=1e-13)
+    # norm_topk_prob off: w = S * s
+    idx3, wt3, _ = oracle.route(x, Wr, b, G, KG, K, S, norm_topk_prob=False)
+    assert np.array_equal(idx3, idx)
+    np.testing.assert_allclose(wt3, S * np.take_along_axis(s, idx, 1), rtol=1e-14)
+    # keeping every group reduces to a plain top-K of the biased scores
+    idx4, _, gap4 = oracle.route(x, Wr, b, G, G, K, S)
+    bb = s + b.astype(np.float64)
+    order = np.argsort(-bb, axis=1, kind="stable")[:, :K]
+    m = gap4 > 1e-9
+    assert np.array_equal(idx4[m], order[m])
+    # with no bias and every group kept, the top-K of b is the top-K of the logits (sigmoid is monotone)
+    idx5, _, gap5 = oracle.route(x, Wr, np.zeros_like(b), G, G, K, S)
+    order = np.argsort(-z, axis=1, kind="stable")[:, :K]
+    m = gap5 > 1e-9
+    assert np.array_equal(idx5[m], order[m])
+    # weights_for on the oracle's own selection reproduces its weights
+    np.testing.assert_allclose(oracle.weights_for(z, idx, S), wt, rtol=1e-15)
+
+
+def test_route_ties_go_to_lower_index():
+    E, G, KG, K, d = 16, 4, 2, 4, 64
+    x = np.zeros((1, d), dtype=np.uint16)          # all logits 0, all scores 0.5
+    Wr = np.zeros((d, E), dtype=np.float32)
+    bias = np.zeros(E, dtype=np.float32)
+    idx, wt, gap = oracle.route(x, Wr, bias, G, KG, K, 2.5)
+    assert idx[0].tolist() == [0, 1, 2, 3]           # groups 0,1 kept; lowest ids first
+    np.testing.assert_allclose(wt[0], 2.5 / 4)
+    assert gap[0] == 0.0
+
+
+# --- dispatch -----------------------------------------------------------------------------
+
+def test_dispatch_matches_stable_argsort():
+    rng = np.random.default_rng(3)
+    for T, K, E in [(1, 1, 4), (7, 3, 16), (300, 8, 256), (1000, 4, 16)]:
+        idx = np.stack([rng.choice(E, K, replace=False) for _ in range(T)]).astype(np.int32)
+        off, sp, pr = oracle.dispatch(idx, E)
+        flat = idx.reshape(-1)
+        assert np.array_equal(sp, np.argsort(flat, kind="stable"))
+        assert np.array_equal(off, np.concatenate([[0], np.cumsum(np.bincount(flat, minlength=E))]))
+        assert np.array_equal(pr[sp], np.arange(T * K))
+        for e in range(E):
+            seg = sp[off[e]:off[e + 1]]
+            assert np.all(flat[seg] == e) and np.all(np.diff(seg) > 0)
+
+
+# --- experts ------------------------------------------------------------------------------
+
+def _expert_torch(x_bits, wg, wu, wd):
+    """SwiGLU expert from torch float64 library ops, h rounded to bf16 by the test's own RNE."""
+    x = torch.from_numpy(_ref.bf16_bits_to_f64(x_bits))
+    g = torch.nn.functional.linear(x, torch.from_numpy(_ref.bf16_bits_to_f64(wg)))
+    u = torch.nn.functional.linear(x, torch.from_numpy(_ref.bf16_bits_to_f64(wu)))
+    a = (torch.nn.functional.silu(g) * u).numpy()
+    h = _ref.bf16_bits_to_f64(_ref.f64_to_bf16_bits_rne(a))
+    return torch.nn.functional.linear(torch.from_numpy(h), torch.from_numpy(_ref.bf16_bits_to_f64(wd))).numpy(), a
+
+
+def test_expert_matches_torch_float64():
+    w = recipes.WORKLOADS[0]
+    x = synth.hidden(w)[:24]
+    wg, wu, wd = synth.expert_weights(w, 5)
+    o = oracle.expert(x, wg, wu, wd)
+    ref, a = _expert_torch(x, wg, wu, wd)
+    # identical up to summation order, unless a lies within rounding noise of a bf16 midpoint
+    rel = np.abs(o - ref).max() / np.sqrt((ref ** 2).mean())
+    assert rel < 1e-12
+
+
+def test_expert_full_shape_one_token():
+    w = recipes.WORKLOADS[2]
+    x = synth.hidden(w, rows=[17])
+    wg, wu, wd = synth.expert_weights(w, 200)
+    o = oracle.expert(x, wg, wu, wd)
+    ref, _ = _expert_torch(x, wg, wu, wd)
+    assert np.abs(o - ref).max() / np.sqrt((ref ** 2).mean()) < 1e-9
+
+
+def test_expert_exact_small_integers():
+    """Inputs that are small integers times powers of two: every sum is exact, so the
+    oracle must match a hand-derivable result bit for bit."""
+    d, I = 8, 4
+    x = _ref.f64_to_bf16_bits_rne(np.array([[1, 2, 0, -1, 0, 0, 3, 0]], dtype=np.float64))
+    wg = np.zeros((I, d)); wu = np.zeros((I, d)); wd = np.zeros((d, I))
+    wg[0, 0] = 1.0; wu[0, 1] = 0.5        # g0 = 1, u0 = 1
+    wg[1, 3] = 2.0; wu[1, 6] = 1.0        # g1 = -2, u1 = 3
+    wg[2, 6] = 0.0; wu[2, 0] = 4.0        # g2 = 0 -> silu 0
+    wg[3, 1] = 0.25; wu[3, 3] = -1.0      # g3 = 0.5, u3 = (-1)(-1) = 1
+    wd[0, 0] = 1.0; wd[1, 1] = 1.0; wd[2, 2] = 1.0; wd[3, 3] = 1.0; wd[4, :] = 1.0
+    to = _ref.f64_to_bf16_bits_rne
+    o = oracle.expert(x, to(wg), to(wu), to(wd))[0]
+    silu = lambda v: v / (1.0 + math.exp(-v))
+    h = [silu(1.0) * 1.0, silu(-2.0) * 3.0, 0.0, silu(0.5) * 1.0]
+    hb = _ref.bf16_bits_to_f64(to(np.array(h)))
+    exp = np.zeros(d)
+    exp[0:4] = hb
+    exp[4] = hb.sum()
+    assert np.array_equal(o, exp)
+
+
+def test_layer_invariants_tiny():
+    w = recipes.WORKLOADS[0]
+    x = synth.hidden(w)
+    Wr = synth.router_weight(w)
+    b = synth.bias(w)
+    wg0, wu0, wd0 = synth.expert_weights(w, 0)
+    E = w.E
+    # identical experts: y = S * expert(x) whatever the routing (weights sum to S)
+    Wg = np.stack([wg0] * E); Wu = np.stack([wu0] * E); Wd = np.stack([wd0] * E)
+    y, idx, wt, gap = oracle.forward(x, Wr, b, Wg, Wu, Wd, w.n_group, w.topk_group, w.top_k, w.scale)
+    one = oracle.expert(x, wg0, wu0, wd0)
+    np.testing.assert_allclose(y, w.scale * one, rtol=0, atol=1e-12 * np.abs(one).max())
+    # gate weights zero: silu(0) = 0, so y = 0 exactly
+    y0, *_ = oracle.forward(x, Wr, b, np.zeros_like(Wg), Wu, Wd, w.n_group, w.topk_group, w.top_k, w.scale)
+    assert np.all(y0 == 0.0)
+    # different experts: doubling every down projection doubles y exactly
+    mats = [synth.expert_weights(w, e) for e in range(E)]
+    Wg = np.stack([m[0] for m in mats]); Wu = np.stack([m[1] for m in mats]); Wd = np.stack([m[2] for m in mats])
+    y1, *_ = oracle.forward(x, Wr, b, Wg, Wu, Wd, w.n_group, w.topk_group, w.top_k, w.scale)
+    Wd2 = _ref.f64_to_bf16_bits_rne(2.0 * _ref.bf16_bits_to_f64(Wd))
+    y2, *_ = oracle.forward(x, Wr, b, Wg, Wu, Wd2, w.n_group, w.topk_group, w.top_k, w.scale)
+    assert np.array_equal(y2, 2.0 * y1)
+    # the layer is the routed sum of single experts (checked per token against the expert routine)
+    for t in (0, 77):
+        acc = np.zeros(w.d)
+        for j in range(w.top_k):
+            e = idx[t, j]
+            acc += wt[t, j] * oracle.expert(x[t:t + 1], Wg[e], Wu[e], Wd[e])[0]
+        np.testing.assert_allclose(y1[t], acc, rtol=0, atol=1e-13 * np.abs(acc).max())
+
+
+# --- RMSNorm ------------------------------------------------------------------------------
+
+def test_rmsnorm_matches_torch_float64():
+    w = recipes.WORKLOADS[4].with_T(16)
+    h = synth.hidden(w)
+    nw = synth.norm_weight(w)
+    x = oracle.rmsnorm(h, nw, w.eps)
+    ht = torch.from_numpy(_ref.bf16_bits_to_f64(h))
+    r = torch.rsqrt(ht.pow(2).mean(-1, keepdim=True) + w.eps)
+    ref = _ref.f64_to_bf16_bits_rne(((ht * r) * torch.from_numpy(_ref.bf16_bits_to_f64(nw))).numpy())
+    diff = np.count_nonzero(x != ref)
+    assert diff <= 2   # rsqrt vs 1/sqrt may differ in the last double bit; a flip needs a midpoint
+    # a constant row normalises to (1/sqrt(1+eps)) * w
+    c = np.full((1, w.d), 0x3F80, dtype=np.uint16)
+    xc = _ref.bf16_bits_to_f64(oracle.rmsnorm(c, nw, w.eps))[0]
+    exp = _ref.bf16_bits_to_f64(_ref.f64_to_bf16_bits_rne(_ref.bf16_bits_to_f64(nw) / math.sqrt(1 + w.eps)))
+    assert np.array_equal(xc, exp)
