@@ -1,0 +1,136 @@
+/*
+ * beam_moe.h -- C ABI of one Beam sparse-MoE layer forward on an MI355X (gfx950).
+ *
+ * The layer (Transformers "Beam" model page, Overview: sparse MoE item and the
+ * FP32 numerics note; archdb "Beam-1.0-501B-A23B" fact sheet, MoE rows;
+ * news.hamidun.com article on Beam, section on where it saves and where it pays
+ * in memory):
+ *   z = x . Wr (FP32), s = sigmoid(z), b = s + bias;
+ *   group score = sum of the two largest b in each group of E/n_group experts;
+ *   keep the topk_group best groups, then the top_k experts by b inside them;
+ *   w_j = routed_scaling_factor * s_j / sum_j s_j   (plain S * s_j if norm_topk_prob = 0);
+ *   y = sum_j w_j * Wd_e . bf16(silu(Wg_e . x) * (Wu_e . x)),   e = chosen expert j.
+ * With the pre-MLP sandwich norm fused in (norm_w != NULL), x = bf16(RMSNorm(h) * norm_w)
+ * first (Transformers "Beam" page, Overview: sandwich norms; BeamConfig: rms_norm_eps).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are caller-owned DEVICE memory, row-major, 16-byte aligned.
+ *     bf16 tensors are raw bfloat16 bit patterns (uint16). The library never
+ *     allocates, frees or synchronises; it keeps no global state and is re-entrant
+ *     when callers use distinct workspaces.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Every launch is queued
+ *     on it; results are ready when that stream reaches the point after the call.
+ *   - Outputs are fully overwritten, never accumulated into.
+ *   - Arguments are validated on the host before anything is launched; a non-OK
+ *     status means nothing was launched (except BEAM_MOE_ERR_HIP, which reports a
+ *     failed launch and may follow earlier launches of the same call).
+ *   - T = 0 returns BEAM_MOE_OK with no launch.
+ *   - Weight layouts follow the (out_features, in_features) convention of linear
+ *     layers: Wg, Wu [E, I, d]; Wd [E, d, I]; the router weight is Wr [d, E] FP32.
+ *
+ * Supported shapes (else BEAM_MOE_ERR_UNSUPPORTED_SHAPE): d and I multiples of 64;
+ * E <= 64, or E in {128, 256, 512, 1024}; E % n_group == 0; n_group <= 64; the
+ * group size E/n_group >= 2 and, per 64-lane wavefront, a power-of-two number of
+ * lanes per group; 1 <= topk_group <= n_group; 1 <= top_k <= min(16, topk_group *
+ * E/n_group); T * top_k < 2^31.
+ */
+#ifndef BEAM_MOE_H
+#define BEAM_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Layer shape and constants (Transformers "Beam" page, BeamConfig: hidden_size = d,
+ * num_experts = E, n_group, topk_group, num_experts_per_tok = top_k,
+ * moe_intermediate_size = I, routed_scaling_factor, norm_topk_prob, rms_norm_eps). */
+typedef struct beam_moe_shape {
+    int64_t T;                    /* tokens in the batch */
+    int32_t d;                    /* hidden size (5120 for Beam) */
+    int32_t E;                    /* routed experts (256) */
+    int32_t n_group;              /* expert groups (8) */
+    int32_t topk_group;           /* groups kept per token (4) */
+    int32_t top_k;                /* experts per token (8) */
+    int32_t I;                    /* expert intermediate size (2560) */
+    float routed_scaling_factor;  /* 2.5 */
+    int32_t norm_topk_prob;       /* 1: renormalise the chosen weights to sum to 1 first */
+    float rms_eps;                /* 1e-6; used only when a norm weight is given */
+} beam_moe_shape;
+
+typedef enum beam_moe_status {
+    BEAM_MOE_OK = 0,
+    BEAM_MOE_ERR_INVALID_ARG = 1,        /* NULL required pointer, misaligned pointer, bad value */
+    BEAM_MOE_ERR_UNSUPPORTED_SHAPE = 2,  /* shape outside the supported set above */
+    BEAM_MOE_ERR_WORKSPACE_TOO_SMALL = 3,
+    BEAM_MOE_ERR_HIP = 4                 /* a kernel launch failed */
+} beam_moe_status;
+
+/* Bytes of device workspace that beam_moe_forward needs for this shape; it also
+ * covers beam_moe_route and beam_moe_dispatch. Returns 0 for an invalid shape. */
+size_t beam_moe_workspace_bytes(const beam_moe_shape* shape);
+
+/* Router: the routing steps of the layer for T tokens.
+ *   x         [T, d] bf16: hidden states (or, with norm_w, the pre-norm hidden states h)
+ *   norm_w    [d] bf16 or NULL: pre-MLP RMSNorm weight; when given, x_normed must be given
+ *   x_normed  [T, d] bf16 out, written iff norm_w != NULL: bf16((h * r) * norm_w),
+ *             r = 1/sqrt(mean(h^2) + rms_eps), computed in FP64
+ *   Wr        [d, E] FP32 router weight;  bias [E] FP32 per-expert selection bias
+ *   topk_idx  [T, top_k] int32 out: chosen experts, by descending biased score,
+ *             ties to the lower expert id
+ *   topk_w    [T, top_k] FP32 out: routing weights aligned with topk_idx (unbiased
+ *             scores, renormalised, times routed_scaling_factor)
+ *   logits    [T, E] FP32 out or NULL: raw router logits z (before the sigmoid)
+ *   workspace, ws_bytes: device scratch of at least beam_moe_workspace_bytes(shape). */
+beam_moe_status beam_moe_route(const beam_moe_shape* shape, const void* x, const void* norm_w, void* x_normed,
+                               const float* Wr, const float* bias, int32_t* topk_idx, float* topk_w,
+                               float* logits, void* workspace, size_t ws_bytes, void* stream);
+
+/* Dispatch: a stable counting sort of the T*top_k (token, slot) pairs by expert
+ * (the single-GPU form of sending each token to the holder of its experts; "Use HF
+ * Transformers" cookbook, Parallelism). Pair p = t*top_k + j.
+ *   topk_idx        [T, top_k] int32: expert ids; each must lie in [0, E) and the ids of
+ *                   one token must be distinct (as beam_moe_route produces). Pairs with an
+ *                   id outside [0, E) are dropped (pair_rank = -1); repeated ids within a
+ *                   token are not detected.
+ *   expert_offsets  [E+1] int32 out: pairs of expert e occupy [offsets[e], offsets[e+1])
+ *   sorted_pairs    [T*top_k] int32 out: pair ids in expert order, ascending p inside an expert
+ *   pair_rank       [T*top_k] int32 out or NULL: position of pair p in sorted_pairs
+ *   workspace, ws_bytes: as for beam_moe_route. */
+beam_moe_status beam_moe_dispatch(const beam_moe_shape* shape, const int32_t* topk_idx, int32_t* expert_offsets,
+                                  int32_t* sorted_pairs, int32_t* pair_rank, void* workspace, size_t ws_bytes,
+                                  void* stream);
+
+/* The whole layer: route, dispatch, the grouped SwiGLU expert GEMMs (BF16 MFMA,
+ * FP32 accumulation, h rounded to bf16 once) and the weighted combine.
+ *   x, norm_w, Wr, bias  as for beam_moe_route (the normed x is kept in the workspace)
+ *   Wg, Wu    [E, I, d] bf16 gate and up projections;  Wd [E, d, I] bf16 down projection
+ *   y         [T, d] FP32 out: sum over the token's experts of w_j * expert output, added
+ *             in slot order j = 0..top_k-1 (bitwise deterministic run to run)
+ *   topk_idx, topk_w, logits: optional copies of the routing (NULL to skip)
+ *   workspace, ws_bytes: at least beam_moe_workspace_bytes(shape). */
+beam_moe_status beam_moe_forward(const beam_moe_shape* shape, const void* x, const void* norm_w, const float* Wr,
+                                 const float* bias, const void* Wg, const void* Wu, const void* Wd, float* y,
+                                 int32_t* topk_idx, float* topk_w, float* logits, void* workspace, size_t ws_bytes,
+                                 void* stream);
+
+/* beam_moe_forward with stage timing, for measurement tools: identical work and results,
+ * plus a hipEventRecord on `stream` of each non-NULL stage_events[i] (hipEvent_t, created
+ * by the caller) at six points: [0] before the router, [1] after the router, [2] after
+ * the dispatch, [3] after the gate/up SwiGLU GEMM, [4] after the down GEMM, [5] after the
+ * combine. stage_events may be NULL (then this is beam_moe_forward). */
+beam_moe_status beam_moe_forward_staged(const beam_moe_shape* shape, const void* x, const void* norm_w,
+                                        const float* Wr, const float* bias, const void* Wg, const void* Wu,
+                                        const void* Wd, float* y, int32_t* topk_idx, float* topk_w, float* logits,
+                                        void* workspace, size_t ws_bytes, void* stream, void* const* stage_events);
+
+/* Static, human-readable name of a status code. */
+const char* beam_moe_status_string(beam_moe_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BEAM_MOE_H */

@@ -19,7 +19,7 @@ _c_i32p = ctypes.POINTER(ctypes.c_int32)
 
 
 def build() -> None:
-    cmd = ["g++", "-O2", "-std=c++17", "-ffp-contract=off", "-fPIC", "-shared", "-pthread",
+    cmd = ["g++", "-O3", "-std=c++17", "-ffp-contract=off", "-fPIC", "-shared", "-pthread",
            os.path.join(_HERE, "beam_oracle.cpp"), "-o", LIB]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:

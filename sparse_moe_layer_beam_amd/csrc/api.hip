@@ -1,0 +1,221 @@
+// C ABI of libbeam_moe.so: argument validation, workspace carving and kernel launches
+// on the caller's stream. Contract and citations: include/beam_moe.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/beam_moe.h"
+#include "kernels.h"
+
+namespace {
+
+using beam::Shape;
+
+bool pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+
+beam_moe_status to_shape(const beam_moe_shape* p, Shape* s) {
+    if (!p) return BEAM_MOE_ERR_INVALID_ARG;
+    if (p->T < 0 || p->d <= 0 || p->E <= 0 || p->n_group <= 0 || p->topk_group <= 0 || p->top_k <= 0 || p->I <= 0)
+        return BEAM_MOE_ERR_INVALID_ARG;
+    if (!std::isfinite(p->routed_scaling_factor) || !std::isfinite(p->rms_eps) || p->rms_eps < 0.0f)
+        return BEAM_MOE_ERR_INVALID_ARG;
+    if (p->E % p->n_group != 0 || p->topk_group > p->n_group) return BEAM_MOE_ERR_INVALID_ARG;
+    const int gsz = p->E / p->n_group;
+    if (p->top_k > p->topk_group * gsz) return BEAM_MOE_ERR_INVALID_ARG;
+    if (p->d % 64 || p->I % 64 || p->top_k > 16 || p->n_group > 64 || gsz < 2) return BEAM_MOE_ERR_UNSUPPORTED_SHAPE;
+    int epl = 1;
+    if (p->E > 64) {
+        if (p->E != 128 && p->E != 256 && p->E != 512 && p->E != 1024) return BEAM_MOE_ERR_UNSUPPORTED_SHAPE;
+        epl = p->E / 64;
+    }
+    if (gsz % epl || !pow2(gsz / epl)) return BEAM_MOE_ERR_UNSUPPORTED_SHAPE;
+    if (p->T * (int64_t)p->top_k >= (int64_t)INT32_MAX) return BEAM_MOE_ERR_UNSUPPORTED_SHAPE;
+    s->T = p->T; s->d = p->d; s->E = p->E; s->G = p->n_group; s->KG = p->topk_group; s->K = p->top_k; s->I = p->I;
+    s->S = p->routed_scaling_factor; s->norm = p->norm_topk_prob ? 1 : 0; s->eps = p->rms_eps;
+    return BEAM_MOE_OK;
+}
+
+bool aligned(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+constexpr size_t kAlign = 256;
+size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Workspace segments, each 256-byte aligned.
+struct Layout {
+    size_t xn, zp, idx, w, cc, ric, off, sp, pr, tiles, ntiles, h, yp, total;
+};
+
+Layout layout(const Shape& s) {
+    const size_t T = (size_t)s.T, P = T * s.K;
+    const size_t n_chunks = (P + beam::kChunkPairs - 1) / beam::kChunkPairs;
+    const size_t max_tiles = (P + 15) / 16 + (size_t)s.E;
+    Layout L{};
+    size_t o = 0;
+    L.xn = o; o += up(T * s.d * 2);
+    L.zp = o; o += up((size_t)beam::router_ksplit(s) * T * s.E * 4);
+    L.idx = o; o += up(P * 4);
+    L.w = o; o += up(P * 4);
+    L.cc = o; o += up(n_chunks * s.E * 4);
+    L.ric = o; o += up(P * 4);
+    L.off = o; o += up(((size_t)s.E + 1) * 4);
+    L.sp = o; o += up(P * 4);
+    L.pr = o; o += up(P * 4);
+    L.tiles = o; o += up(max_tiles * 2 * 4);
+    L.ntiles = o; o += up(4);
+    L.h = o; o += up(P * s.I * 2);
+    L.yp = o; o += up(P * s.d * 4);
+    L.total = o;
+    return L;
+}
+
+template <class T>
+T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
+
+beam_moe_status hip_status() { return hipGetLastError() == hipSuccess ? BEAM_MOE_OK : BEAM_MOE_ERR_HIP; }
+
+// Router into caller-visible buffers; x_in is already normed when a norm weight is used.
+void run_route(const Shape& s, const Layout& L, const void* x, const void* norm_w, void* x_normed, const float* Wr,
+               const float* bias, int32_t* idx, float* w, float* logits, void* ws, hipStream_t st) {
+    const void* xin = x;
+    if (norm_w) {
+        beam::launch_rmsnorm(s, x, norm_w, x_normed, st);
+        xin = x_normed;
+    }
+    const int ks = beam::router_ksplit(s);
+    float* zp = at<float>(ws, L.zp);
+    beam::launch_router_logits(s, xin, Wr, zp, ks, st);
+    beam::launch_router_topk(s, zp, ks, bias, idx, w, logits, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t beam_moe_workspace_bytes(const beam_moe_shape* shape) {
+    Shape s;
+    if (to_shape(shape, &s) != BEAM_MOE_OK) return 0;
+    return layout(s).total;
+}
+
+beam_moe_status beam_moe_route(const beam_moe_shape* shape, const void* x, const void* norm_w, void* x_normed,
+                               const float* Wr, const float* bias, int32_t* topk_idx, float* topk_w, float* logits,
+                               void* workspace, size_t ws_bytes, void* stream) {
+    Shape s;
+    beam_moe_status st = to_shape(shape, &s);
+    if (st != BEAM_MOE_OK) return st;
+    if (!x || !Wr || !bias || !topk_idx || !topk_w || (norm_w && !x_normed)) return BEAM_MOE_ERR_INVALID_ARG;
+    if (!aligned(x) || !aligned(Wr) || !aligned(bias) || !aligned(topk_idx) || !aligned(topk_w) ||
+        (norm_w && (!aligned(norm_w) || !aligned(x_normed))) || (logits && !aligned(logits)))
+        return BEAM_MOE_ERR_INVALID_ARG;
+    if (s.T == 0) return BEAM_MOE_OK;
+    const Layout L = layout(s);
+    if (!workspace || !aligned(workspace)) return BEAM_MOE_ERR_INVALID_ARG;
+    if (ws_bytes < L.total) return BEAM_MOE_ERR_WORKSPACE_TOO_SMALL;
+    (void)hipGetLastError();
+    run_route(s, L, x, norm_w, x_normed, Wr, bias, topk_idx, topk_w, logits, workspace, (hipStream_t)stream);
+    return hip_status();
+}
+
+beam_moe_status beam_moe_dispatch(const beam_moe_shape* shape, const int32_t* topk_idx, int32_t* expert_offsets,
+                                  int32_t* sorted_pairs, int32_t* pair_rank, void* workspace, size_t ws_bytes,
+                                  void* stream) {
+    Shape s;
+    beam_moe_status st = to_shape(shape, &s);
+    if (st != BEAM_MOE_OK) return st;
+    if (!topk_idx || !expert_offsets || !sorted_pairs) return BEAM_MOE_ERR_INVALID_ARG;
+    if (!aligned(topk_idx) || !aligned(expert_offsets) || !aligned(sorted_pairs) || (pair_rank && !aligned(pair_rank)))
+        return BEAM_MOE_ERR_INVALID_ARG;
+    if (s.T == 0) return BEAM_MOE_OK;
+    const Layout L = layout(s);
+    if (!workspace || !aligned(workspace)) return BEAM_MOE_ERR_INVALID_ARG;
+    if (ws_bytes < L.total) return BEAM_MOE_ERR_WORKSPACE_TOO_SMALL;
+    (void)hipGetLastError();
+    beam::launch_dispatch(s, topk_idx, expert_offsets, sorted_pairs, pair_rank, at<int32_t>(workspace, L.cc),
+                          at<int32_t>(workspace, L.ric), nullptr, nullptr, 16, (hipStream_t)stream);
+    return hip_status();
+}
+
+}  // extern "C"
+
+namespace {
+
+beam_moe_status forward_impl(const beam_moe_shape* shape, const void* x, const void* norm_w, const float* Wr,
+                             const float* bias, const void* Wg, const void* Wu, const void* Wd, float* y,
+                             int32_t* topk_idx, float* topk_w, float* logits, void* workspace, size_t ws_bytes,
+                             void* stream, void* const* events) {
+    Shape s;
+    beam_moe_status st = to_shape(shape, &s);
+    if (st != BEAM_MOE_OK) return st;
+    if (!x || !Wr || !bias || !Wg || !Wu || !Wd || !y) return BEAM_MOE_ERR_INVALID_ARG;
+    if (!aligned(x) || !aligned(Wr) || !aligned(bias) || !aligned(Wg) || !aligned(Wu) || !aligned(Wd) || !aligned(y) ||
+        (norm_w && !aligned(norm_w)) || (topk_idx && !aligned(topk_idx)) || (topk_w && !aligned(topk_w)) ||
+        (logits && !aligned(logits)))
+        return BEAM_MOE_ERR_INVALID_ARG;
+    if (s.T == 0) return BEAM_MOE_OK;
+    const Layout L = layout(s);
+    if (!workspace || !aligned(workspace)) return BEAM_MOE_ERR_INVALID_ARG;
+    if (ws_bytes < L.total) return BEAM_MOE_ERR_WORKSPACE_TOO_SMALL;
+    hipStream_t hs = (hipStream_t)stream;
+    (void)hipGetLastError();
+    auto mark = [&](int i) {
+        if (events && events[i]) (void)hipEventRecord((hipEvent_t)events[i], hs);
+    };
+    int32_t* idx = topk_idx ? topk_idx : at<int32_t>(workspace, L.idx);
+    float* w = topk_w ? topk_w : at<float>(workspace, L.w);
+    void* xn = at<void>(workspace, L.xn);
+    mark(0);
+    run_route(s, L, x, norm_w, xn, Wr, bias, idx, w, logits, workspace, hs);
+    mark(1);
+    const void* xin = norm_w ? xn : x;
+    int32_t* off = at<int32_t>(workspace, L.off);
+    int32_t* sp = at<int32_t>(workspace, L.sp);
+    int32_t* pr = at<int32_t>(workspace, L.pr);
+    int32_t* tiles = at<int32_t>(workspace, L.tiles);
+    int32_t* ntiles = at<int32_t>(workspace, L.ntiles);
+    beam::launch_dispatch(s, idx, off, sp, pr, at<int32_t>(workspace, L.cc), at<int32_t>(workspace, L.ric), tiles,
+                          ntiles, beam::experts_tile_m(s), hs);
+    mark(2);
+    void* h = at<void>(workspace, L.h);
+    float* yp = at<float>(workspace, L.yp);
+    beam::launch_swiglu(s, xin, off, sp, tiles, ntiles, Wg, Wu, h, hs);
+    mark(3);
+    beam::launch_down(s, h, off, sp, w, tiles, ntiles, Wd, yp, hs);
+    mark(4);
+    beam::launch_combine(s, yp, pr, y, hs);
+    mark(5);
+    return hip_status();
+}
+
+}  // namespace
+
+extern "C" {
+
+beam_moe_status beam_moe_forward(const beam_moe_shape* shape, const void* x, const void* norm_w, const float* Wr,
+                                 const float* bias, const void* Wg, const void* Wu, const void* Wd, float* y,
+                                 int32_t* topk_idx, float* topk_w, float* logits, void* workspace, size_t ws_bytes,
+                                 void* stream) {
+    return forward_impl(shape, x, norm_w, Wr, bias, Wg, Wu, Wd, y, topk_idx, topk_w, logits, workspace, ws_bytes,
+                        stream, nullptr);
+}
+
+beam_moe_status beam_moe_forward_staged(const beam_moe_shape* shape, const void* x, const void* norm_w,
+                                        const float* Wr, const float* bias, const void* Wg, const void* Wu,
+                                        const void* Wd, float* y, int32_t* topk_idx, float* topk_w, float* logits,
+                                        void* workspace, size_t ws_bytes, void* stream, void* const* stage_events) {
+    return forward_impl(shape, x, norm_w, Wr, bias, Wg, Wu, Wd, y, topk_idx, topk_w, logits, workspace, ws_bytes,
+                        stream, stage_events);
+}
+
+const char* beam_moe_status_string(beam_moe_status status) {
+    switch (status) {
+        case BEAM_MOE_OK: return "ok";
+        case BEAM_MOE_ERR_INVALID_ARG: return "invalid argument";
+        case BEAM_MOE_ERR_UNSUPPORTED_SHAPE: return "unsupported shape";
+        case BEAM_MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+        case BEAM_MOE_ERR_HIP: return "HIP launch failure";
+    }
+    return "unknown status";
+}
+
+}  // extern "C"

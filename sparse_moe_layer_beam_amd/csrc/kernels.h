@@ -1,0 +1,40 @@
+// Host-side launchers of the MoE-layer kernels (internal to libbeam_moe.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace beam {
+
+struct Shape {
+    int64_t T;
+    int d, E, G, KG, K, I;
+    float S;
+    int norm;
+    float eps;
+};
+
+// Router (router.hip)
+void launch_rmsnorm(const Shape& s, const void* h, const void* w, void* x_out, hipStream_t st);
+int router_ksplit(const Shape& s);
+void launch_router_logits(const Shape& s, const void* x, const float* Wr, float* z_part, int ks, hipStream_t st);
+void launch_router_topk(const Shape& s, const float* z_part, int ks, const float* bias, int32_t* idx, float* w,
+                        float* logits, hipStream_t st);
+
+// Dispatch (dispatch.hip)
+constexpr int kChunkPairs = 1024;
+void launch_dispatch(const Shape& s, const int32_t* idx, int32_t* offsets, int32_t* sorted_pairs,
+                     int32_t* pair_rank, int32_t* chunk_counts, int32_t* rank_in_chunk, int32_t* tiles,
+                     int32_t* n_tiles, int tile_m, hipStream_t st);
+
+// Experts (experts.hip)
+int experts_tile_m(const Shape& s);
+void launch_swiglu(const Shape& s, const void* x, const int32_t* offsets, const int32_t* sorted_pairs,
+                   const int32_t* tiles, const int32_t* n_tiles, const void* Wg, const void* Wu, void* h,
+                   hipStream_t st);
+void launch_down(const Shape& s, const void* h, const int32_t* offsets, const int32_t* sorted_pairs,
+                 const float* topk_w, const int32_t* tiles, const int32_t* n_tiles, const void* Wd, float* y_perm,
+                 hipStream_t st);
+void launch_combine(const Shape& s, const float* y_perm, const int32_t* pair_rank, float* y, hipStream_t st);
+
+}  // namespace beam

@@ -1,0 +1,251 @@
+// Router of the Beam MoE layer: optional pre-MLP RMSNorm, FP32 router GEMM,
+// sigmoid + bias, group-limited top-k and weight normalisation.
+//
+// Method: Transformers "Beam" model page (Overview: sparse MoE item, sandwich norms,
+// FP32 numerics note; BeamConfig: n_group, topk_group, num_experts_per_tok,
+// norm_topk_prob, routed_scaling_factor, rms_norm_eps) and archdb
+// "Beam-1.0-501B-A23B" fact sheet (MoE: sigmoid gating, group score = sum of the
+// top-2 biased scores, renormalised weights, 2.5 scaling).
+#include "common.h"
+#include "kernels.h"
+
+namespace beam {
+namespace {
+
+// ---------------------------------------------------------------------------------------
+// Pre-MLP RMSNorm, one 256-thread block per token. Done in FP64 (the pages ask for at
+// least FP32): the bf16 rounding of x is then a function of h and w alone, independent
+// of the reduction order, so every consumer of x sees the same bits.
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const u16* __restrict__ h, const u16* __restrict__ w,
+                                                      u16* __restrict__ x, int d, double eps) {
+    const int64_t t = blockIdx.x;
+    const u16* hr = h + t * d;
+    double ss = 0.0;
+    for (int c = threadIdx.x * 8; c < d; c += 256 * 8) {
+        uint4 v = *reinterpret_cast<const uint4*>(hr + c);
+        uint32_t p[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            double a = bf16_to_f32((u16)(p[i] & 0xffffu)), b = bf16_to_f32((u16)(p[i] >> 16));
+            ss += a * a;
+            ss += b * b;
+        }
+    }
+    ss = wave_sum_f64(ss);
+    __shared__ double part[4];
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    ss = part[0] + part[1] + part[2] + part[3];
+    const double r = 1.0 / sqrt(ss / (double)d + eps);
+    for (int c = threadIdx.x * 8; c < d; c += 256 * 8) {
+        uint4 v = *reinterpret_cast<const uint4*>(hr + c);
+        uint4 g = *reinterpret_cast<const uint4*>(w + c);
+        uint32_t p[4] = {v.x, v.y, v.z, v.w}, q[4] = {g.x, g.y, g.z, g.w}, o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            double a0 = bf16_to_f32((u16)(p[i] & 0xffffu)), a1 = bf16_to_f32((u16)(p[i] >> 16));
+            double w0 = bf16_to_f32((u16)(q[i] & 0xffffu)), w1 = bf16_to_f32((u16)(q[i] >> 16));
+            u16 lo = f64_to_bf16((a0 * r) * w0), hi = f64_to_bf16((a1 * r) * w1);
+            o[i] = (uint32_t)lo | ((uint32_t)hi << 16);
+        }
+        *reinterpret_cast<uint4*>(x + t * d + c) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Router GEMM z = x . Wr in FP32 on the vector ALUs. Block tile: 64 tokens x 64 experts,
+// K staged through LDS in steps of 32; each thread owns a 4x4 register tile. blockIdx.z
+// splits K so that a decode-sized batch still spreads the 5 MB of Wr over many CUs; the
+// partial sums go to z_part[ks] and are added in fixed order by the top-k kernel.
+constexpr int RT = 64, RE = 64, RK = 32;
+
+__global__ __launch_bounds__(256) void router_logits_kernel(const u16* __restrict__ x, const float* __restrict__ Wr,
+                                                            float* __restrict__ zp, int64_t T, int d, int E,
+                                                            int kchunk) {
+    __shared__ float xs[RK][RT + 4];
+    __shared__ float ws[RK][RE + 4];
+    const int64_t t0 = (int64_t)blockIdx.x * RT;
+    const int e0 = blockIdx.y * RE;
+    const int kb = blockIdx.z * kchunk, ke = kb + kchunk;
+    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+    float acc[4][4] = {};
+    for (int k0 = kb; k0 < ke; k0 += RK) {
+        {
+            const int tok = threadIdx.x >> 2, kc = (threadIdx.x & 3) * 8;
+            const int64_t t = t0 + tok;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (t < T) v = *reinterpret_cast<const uint4*>(x + t * d + k0 + kc);
+            uint32_t p[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                xs[kc + 2 * i][tok] = bf16_to_f32((u16)(p[i] & 0xffffu));
+                xs[kc + 2 * i + 1][tok] = bf16_to_f32((u16)(p[i] >> 16));
+            }
+        }
+        {
+            const int kk = threadIdx.x >> 3, ec = (threadIdx.x & 7) * 8;
+            const float* src = Wr + (int64_t)(k0 + kk) * E + e0 + ec;
+            if ((E & 3) == 0 && e0 + ec + 8 <= E) {
+                float4 a = *reinterpret_cast<const float4*>(src);
+                float4 b = *reinterpret_cast<const float4*>(src + 4);
+                ws[kk][ec + 0] = a.x; ws[kk][ec + 1] = a.y; ws[kk][ec + 2] = a.z; ws[kk][ec + 3] = a.w;
+                ws[kk][ec + 4] = b.x; ws[kk][ec + 5] = b.y; ws[kk][ec + 6] = b.z; ws[kk][ec + 7] = b.w;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) ws[kk][ec + i] = (e0 + ec + i < E) ? src[i] : 0.0f;
+            }
+        }
+        __syncthreads();
+#pragma unroll 8
+        for (int k = 0; k < RK; ++k) {
+            float a[4], b[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) { a[i] = xs[k][4 * ty + i]; b[i] = ws[k][4 * tx + i]; }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+        }
+        __syncthreads();
+    }
+    float* out = zp + (int64_t)blockIdx.z * T * E;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t t = t0 + 4 * ty + i;
+        if (t >= T) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e = e0 + 4 * tx + j;
+            if (e < E) out[t * E + e] = acc[i][j];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Selection, one wavefront per token. Lane l holds experts [l*EPL, (l+1)*EPL); a group of
+// E/G experts spans LPG = E/(G*EPL) adjacent lanes (a power of two), so the group top-2
+// is an xor-butterfly inside aligned lane blocks. Ties go to the lower index everywhere.
+template <int EPL>
+__global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ zp, int ks, int64_t T, int E,
+                                                          int G, int KG, int K, float S, int norm,
+                                                          const float* __restrict__ bias, int32_t* __restrict__ idx,
+                                                          float* __restrict__ wout, float* __restrict__ logits) {
+    const int lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const int e0 = lane * EPL;
+    const bool live = e0 < E;
+    const float NEG = -INFINITY;
+    float s[EPL], b[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const int e = e0 + i;
+        s[i] = 0.0f;
+        b[i] = NEG;
+        if (e < E) {
+            float z = 0.0f;
+            for (int q = 0; q < ks; ++q) z += zp[((int64_t)q * T + t) * E + e];
+            if (logits) logits[t * E + e] = z;
+            s[i] = 1.0f / (1.0f + expf(-z));
+            b[i] = s[i] + bias[e];
+        }
+    }
+    // Group score: sum of the two largest biased scores of the group.
+    const int gsz = E / G;
+    const int lpg = gsz / EPL;
+    float v1 = NEG, v2 = NEG;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const float v = b[i];
+        if (v > v1) { v2 = v1; v1 = v; } else if (v > v2) { v2 = v; }
+    }
+    for (int m = 1; m < lpg; m <<= 1) {
+        const float o1 = __shfl_xor(v1, m, kWave), o2 = __shfl_xor(v2, m, kWave);
+        const float n2 = fmaxf(fminf(v1, o1), fmaxf(v2, o2));
+        v1 = fmaxf(v1, o1);
+        v2 = n2;
+    }
+    const float gs = v1 + v2;
+    // Lane g < G takes group g's score, then its rank among the groups.
+    const float gsl = __shfl(gs, (lane < G ? lane : 0) * lpg, kWave);
+    int rank = 0;
+    for (int g2 = 0; g2 < G; ++g2) {
+        const float o = __shfl(gsl, g2, kWave);
+        rank += (o > gsl) || (o == gsl && g2 < lane);
+    }
+    const uint64_t kept = __ballot(lane < G && rank < KG);
+    const bool my_kept = live && ((kept >> (e0 / gsz)) & 1ull);
+    // Top-K among experts of the kept groups: K rounds of a wave-wide argmax on a key
+    // that orders by biased score, then by lower expert id.
+    uint64_t key[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const int e = e0 + i;
+        key[i] = (my_kept && e < E) ? (((uint64_t)f32_order_key(b[i]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e))
+                                    : 0ull;
+    }
+    float sum = 0.0f, my_s = 0.0f;
+    int my_e = 0;
+    for (int j = 0; j < K; ++j) {
+        uint64_t best = 0;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) best = key[i] > best ? key[i] : best;
+        best = wave_max_u64(best);
+        const int e = (int)(0xffffffffu - (uint32_t)(best & 0xffffffffu));
+        float se = 0.0f;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i)
+            if (e0 + i == e) { se = s[i]; key[i] = 0ull; }
+        se = __shfl(se, e / EPL, kWave);
+        sum += se;
+        if (lane == j) { my_e = e; my_s = se; }
+    }
+    if (lane < K) {
+        idx[t * K + lane] = my_e;
+        wout[t * K + lane] = norm ? S * my_s / sum : S * my_s;
+    }
+}
+
+}  // namespace
+
+void launch_rmsnorm(const Shape& s, const void* h, const void* w, void* x_out, hipStream_t st) {
+    hipLaunchKernelGGL(rmsnorm_kernel, dim3((unsigned)s.T), dim3(256), 0, st, (const u16*)h, (const u16*)w,
+                       (u16*)x_out, s.d, (double)s.eps);
+}
+
+int router_ksplit(const Shape& s) {
+    const int64_t tiles = (int64_t)((s.E + RE - 1) / RE) * ((s.T + RT - 1) / RT);
+    int64_t want = 512 / (tiles > 0 ? tiles : 1);
+    if (want < 1) want = 1;
+    if (want > 16) want = 16;
+    const int steps = s.d / RK;
+    int ks = 1;
+    for (int c = 1; c <= want; ++c)
+        if (steps % c == 0) ks = c;
+    return ks;
+}
+
+void launch_router_logits(const Shape& s, const void* x, const float* Wr, float* z_part, int ks, hipStream_t st) {
+    dim3 grid((unsigned)((s.T + RT - 1) / RT), (unsigned)((s.E + RE - 1) / RE), (unsigned)ks);
+    hipLaunchKernelGGL(router_logits_kernel, grid, dim3(256), 0, st, (const u16*)x, Wr, z_part, s.T, s.d, s.E,
+                       s.d / ks);
+}
+
+void launch_router_topk(const Shape& s, const float* z_part, int ks, const float* bias, int32_t* idx, float* w,
+                        float* logits, hipStream_t st) {
+    dim3 grid((unsigned)((s.T + 3) / 4));
+    const int epl = s.E <= 64 ? 1 : s.E / 64;
+#define BEAM_TOPK(N)                                                                                              \
+    hipLaunchKernelGGL(router_topk_kernel<N>, grid, dim3(256), 0, st, z_part, ks, s.T, s.E, s.G, s.KG, s.K, s.S, \
+                       s.norm, bias, idx, w, logits)
+    switch (epl) {
+        case 1: BEAM_TOPK(1); break;
+        case 2: BEAM_TOPK(2); break;
+        case 4: BEAM_TOPK(4); break;
+        case 8: BEAM_TOPK(8); break;
+        default: BEAM_TOPK(16); break;
+    }
+#undef BEAM_TOPK
+}
+
+}  // namespace beam

@@ -1,0 +1,132 @@
+"""The C ABI without a GPU: the library loads, exports what include/beam_moe.h
+declares, and rejects bad arguments on the host before launching anything.
+
+Every call here either fails validation or has T = 0, so no kernel is ever
+launched (the fake pointers below are never dereferenced)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import sparse_moe_layer_beam_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "beam_moe.h")
+
+OK, INVALID, UNSUPPORTED, WS_SMALL = (moe.BEAM_MOE_OK, moe.BEAM_MOE_ERR_INVALID_ARG,
+                                      moe.BEAM_MOE_ERR_UNSUPPORTED_SHAPE, moe.BEAM_MOE_ERR_WORKSPACE_TOO_SMALL)
+A = 1 << 20          # a 16-byte-aligned fake device address (never dereferenced)
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(beam_moe_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_names():
+    assert _declared() == sorted(moe.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    L = moe.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", moe.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (beam_moe_\w+)", out))
+    assert set(_declared()) <= exported
+
+
+def test_shape_struct_matches_header_layout():
+    assert ctypes.sizeof(moe.beam_moe_shape) == 48
+    assert moe.beam_moe_shape.routed_scaling_factor.offset == 32
+    assert moe.beam_moe_shape.rms_eps.offset == 40
+
+
+def beam(T=64, **kw):
+    args = dict(T=T, d=5120, E=256, n_group=8, topk_group=4, top_k=8, I=2560)
+    args.update(kw)
+    return moe.make_shape(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), OK),
+    (dict(T=-1), INVALID),
+    (dict(d=0), INVALID),
+    (dict(E=250), INVALID),            # not divisible by n_group
+    (dict(topk_group=9), INVALID),
+    (dict(top_k=129), INVALID),        # more than topk_group * group size
+    (dict(d=5000), UNSUPPORTED),       # not a multiple of 64
+    (dict(I=2500), UNSUPPORTED),
+    (dict(top_k=17, topk_group=8), UNSUPPORTED),
+    (dict(E=96, n_group=8), UNSUPPORTED),
+    (dict(E=2048, n_group=8), UNSUPPORTED),
+    (dict(E=256, n_group=256, topk_group=4, top_k=4), UNSUPPORTED),   # group of one expert
+    (dict(E=256, n_group=128, topk_group=4), UNSUPPORTED),   # more than 64 groups
+    (dict(E=24, n_group=4, topk_group=2, top_k=4), UNSUPPORTED),  # 6 lanes per group
+    (dict(T=1 << 28), UNSUPPORTED),    # T * top_k overflows int32 pair ids
+])
+def test_shape_validation(kw, status):
+    s = beam(**kw)
+    nbytes = moe.beam_moe_workspace_bytes(s)
+    assert (nbytes > 0) == (status == OK)
+    st = moe.beam_moe_forward(s, A, None, A, A, A, A, A, A, None, None, None, None, stream=0, check=False)
+    # with a valid shape the missing workspace is what is reported
+    assert st == (INVALID if status == OK else status)
+
+
+def test_workspace_size_grows_with_T_and_is_enough_for_all_entry_points():
+    sizes = [moe.beam_moe_workspace_bytes(beam(T)) for T in (1, 64, 8192, 32768)]
+    assert sizes == sorted(sizes) and sizes[0] > 0
+    # y_perm (T*K*d fp32) and h (T*K*I bf16) dominate the forward workspace
+    assert sizes[3] >= 32768 * 8 * (5120 * 4 + 2560 * 2)
+
+
+def test_null_and_misaligned_pointers_are_rejected():
+    s = beam()
+    n = moe.beam_moe_workspace_bytes(s)
+
+    class WS:  # fake workspace object: only its address and byte size are read
+        def __init__(self, ptr, nbytes):
+            self.p, self.n = ptr, nbytes
+
+        def data_ptr(self):
+            return self.p
+
+        def numel(self):
+            return self.n
+
+        def element_size(self):
+            return 1
+
+    ws_small = WS(A, n - 1)
+    ws_misaligned = WS(A + 8, n)
+    f = lambda *a: moe.beam_moe_forward(s, *a, stream=0, check=False)
+    assert f(A, None, A, A, A, A, A, A, None, None, None, ws_small) == WS_SMALL
+    assert f(A, None, A, A, A, A, A, A, None, None, None, ws_misaligned) == INVALID
+    assert f(None, None, A, A, A, A, A, A, None, None, None, ws_small) == INVALID      # x missing
+    assert f(A, None, A, A, A, A, None, A, None, None, None, ws_small) == INVALID      # Wd missing
+    assert f(A + 2, None, A, A, A, A, A, A, None, None, None, ws_small) == INVALID     # misaligned x
+    assert f(A, None, A, A, A, A, A, A, A + 4, None, None, ws_small) == INVALID        # misaligned idx
+    r = lambda *a: moe.beam_moe_route(s, *a, stream=0, check=False)
+    assert r(A, A, None, A, A, A, A, None, ws_small) == INVALID        # norm weight without x_normed
+    assert r(A, None, None, A, A, A, A, None, ws_small) == WS_SMALL
+    d = lambda *a: moe.beam_moe_dispatch(s, *a, stream=0, check=False)
+    assert d(A, A, None, None, ws_small) == INVALID                    # sorted_pairs missing
+    assert d(A, A, A, None, ws_small) == WS_SMALL
+    with pytest.raises(moe.BeamMoeError):
+        moe.beam_moe_dispatch(s, A, A, A, None, ws_small, stream=0)
+
+
+def test_zero_tokens_returns_ok_without_workspace():
+    s = beam(T=0)
+    assert moe.beam_moe_forward(s, A, None, A, A, A, A, A, A, None, None, None, None, stream=0, check=False) == OK
+    assert moe.beam_moe_route(s, A, None, None, A, A, A, A, None, None, stream=0, check=False) == OK
+    assert moe.beam_moe_dispatch(s, A, A, A, None, None, stream=0, check=False) == OK
+
+
+def test_status_strings():
+    assert moe.beam_moe_status_string(OK) == "ok"
+    assert "workspace" in moe.beam_moe_status_string(WS_SMALL)
+    assert moe.beam_moe_status_string(99) == "unknown status"
