@@ -17,18 +17,97 @@
 namespace beam {
 namespace {
 
+#ifndef BEAM_GU_DEPTH
+#define BEAM_GU_DEPTH 8         // gate/up: k-steps of 32 prefetched ahead of the MFMAs
+#endif
+#ifndef BEAM_DN_DEPTH
+#define BEAM_DN_DEPTH 4         // down: the same
+#endif
+#ifndef BEAM_STREAM_MT
+#define BEAM_STREAM_MT 1        // 16-token tiles per pass over an expert's weights
+#endif
+#ifndef BEAM_STREAM_PIN
+#define BEAM_STREAM_PIN 0       // 1: forbid scheduling across ring steps
+#endif
+#ifndef BEAM_STREAM_NT
+#define BEAM_STREAM_NT 0        // 1: non-temporal weight loads
+#endif
+
 constexpr int kWavesPerBlock = 4;
-constexpr int kChanPerWave = 32;   // two 16-channel MFMA tiles
-constexpr int kMT = 4;             // 16-token tiles held in registers per pass
+constexpr int kDgu = BEAM_GU_DEPTH;
+constexpr int kDdn = BEAM_DN_DEPTH;
+constexpr int kMT = BEAM_STREAM_MT;
+constexpr bool kNT = BEAM_STREAM_NT != 0;
 
 __device__ __forceinline__ bf16x8 ld8(const u16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+
+template <bool NT>
+__device__ __forceinline__ bf16x8 ldw(const u16* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(p));
+    else return ld8(p);
+}
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// acc[m][r] += A_r . B_m^T over k in [0, K): A_r = 16 weight rows (lane: row r16, k-chunk kq),
+// B_m = 16 token rows. Weights and token fragments live in a ring of D register slots: slot s
+// is consumed by its MFMAs and then refilled with the step D ahead, so every wave keeps
+// D*(RB+MT) 16-byte loads in flight without register copies. Prefetch addresses past the end
+// are clamped to the last step (a redundant, in-bounds load that is never consumed); the
+// (K/32) % D leftover steps are taken from the ring after the main loop.
+template <int RB, int MT, int D, bool NT>
+__device__ __forceinline__ void stream_core(const u16* const (&a)[RB], const u16* const (&b)[MT], int K,
+                                            f32x4 (&acc)[MT][RB]) {
+    bf16x8 wa[D][RB], xb[D][MT];
+    const int last = K - 32;
+    const int nsteps = K / 32;
+    const int kfull = (nsteps - nsteps % D) * 32;
+#pragma unroll
+    for (int s = 0; s < D; ++s) {
+        const int k = min(s * 32, last);
+#pragma unroll
+        for (int r = 0; r < RB; ++r) wa[s][r] = ldw<NT>(a[r] + k);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) xb[s][m] = ld8(b[m] + k);
+        if constexpr (BEAM_STREAM_PIN != 0) __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int k0 = 0; k0 < kfull; k0 += 32 * D) {
+#pragma unroll
+        for (int s = 0; s < D; ++s) {
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int r = 0; r < RB; ++r) acc[m][r] = mfma16(wa[s][r], xb[s][m], acc[m][r]);
+            const int kn = min(k0 + (s + D) * 32, last);
+#pragma unroll
+            for (int r = 0; r < RB; ++r) wa[s][r] = ldw<NT>(a[r] + kn);
+#pragma unroll
+            for (int m = 0; m < MT; ++m) xb[s][m] = ld8(b[m] + kn);
+            if constexpr (BEAM_STREAM_PIN != 0) __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    const int rem = nsteps - kfull / 32;
+#pragma unroll
+    for (int s = 0; s < D; ++s)
+        if (s < rem)
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int r = 0; r < RB; ++r) acc[m][r] = mfma16(wa[s][r], xb[s][m], acc[m][r]);
+}
+
+template <int MT>
+__device__ __forceinline__ void zero_acc(f32x4 (&acc)[MT][1]) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[m][0] = f32x4{0, 0, 0, 0};
+}
+
 // h[beg+m, n] = bf16(silu(x_m . Wg[e,n]) * (x_m . Wu[e,n])) for the tokens m of expert e.
-// grid: (ceil(I / 128), E); block: 4 waves, each owning 32 output channels.
+// grid: (ceil(I / 64), E); block: 4 waves, each owning 16 output channels. A wave streams
+// its 16 gate rows, then its 16 up rows: one 16-row stream at a time keeps the number of
+// DRAM rows open across the chip low, which is what sets the achieved bandwidth here.
 __global__ __launch_bounds__(256) void swiglu_stream_kernel(const u16* __restrict__ x,
                                                             const int32_t* __restrict__ offsets,
                                                             const int32_t* __restrict__ sorted_pairs, int K,
@@ -39,13 +118,11 @@ __global__ __launch_bounds__(256) void swiglu_stream_kernel(const u16* __restric
     const int n_e = offsets[e + 1] - beg;
     if (n_e <= 0) return;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int n0 = (blockIdx.x * kWavesPerBlock + wave) * kChanPerWave;
+    const int n0 = (blockIdx.x * kWavesPerBlock + wave) * 16;
     if (n0 >= I) return;
     const int r16 = lane & 15, kq = (lane >> 4) * 8;
-    const u16* g0 = Wg + ((size_t)e * I + n0 + r16) * d + kq;
-    const u16* g1 = g0 + (size_t)16 * d;
-    const u16* u0 = Wu + ((size_t)e * I + n0 + r16) * d + kq;
-    const u16* u1 = u0 + (size_t)16 * d;
+    const u16* const ag[1] = {Wg + ((size_t)e * I + n0 + r16) * d + kq};
+    const u16* const au[1] = {Wu + ((size_t)e * I + n0 + r16) * d + kq};
     for (int mb = 0; mb < n_e; mb += 16 * kMT) {
         const int ntile = min(kMT, (n_e - mb + 15) / 16);
         const u16* xp[kMT];
@@ -54,45 +131,29 @@ __global__ __launch_bounds__(256) void swiglu_stream_kernel(const u16* __restric
             const int m = min(mb + 16 * mt + r16, n_e - 1);   // rows past the end read a valid row; discarded
             xp[mt] = x + (size_t)(sorted_pairs[beg + m] / K) * d + kq;
         }
-        f32x4 ag[kMT][2], au[kMT][2];
-#pragma unroll
-        for (int mt = 0; mt < kMT; ++mt)
-#pragma unroll
-            for (int r = 0; r < 2; ++r) { ag[mt][r] = f32x4{0, 0, 0, 0}; au[mt][r] = f32x4{0, 0, 0, 0}; }
-#pragma unroll 2
-        for (int k = 0; k < d; k += 32) {
-            const bf16x8 wg0 = ld8(g0 + k), wg1 = ld8(g1 + k), wu0 = ld8(u0 + k), wu1 = ld8(u1 + k);
-#pragma unroll
-            for (int mt = 0; mt < kMT; ++mt) {
-                if (mt < ntile) {
-                    const bf16x8 xb = ld8(xp[mt] + k);
-                    ag[mt][0] = mfma16(wg0, xb, ag[mt][0]);
-                    ag[mt][1] = mfma16(wg1, xb, ag[mt][1]);
-                    au[mt][0] = mfma16(wu0, xb, au[mt][0]);
-                    au[mt][1] = mfma16(wu1, xb, au[mt][1]);
-                }
-            }
-        }
-        // lane holds channels n0 + 16r + 4*(lane/16) + i for token row mb + 16*mt + lane%16
+        f32x4 g[kMT][1], u[kMT][1];
+        zero_acc<kMT>(g);
+        zero_acc<kMT>(u);
+        stream_core<1, kMT, kDgu, kNT>(ag, xp, d, g);
+        stream_core<1, kMT, kDgu, kNT>(au, xp, d, u);
+        // lane holds channels n0 + 4*(lane/16) + i for token row mb + 16*mt + lane%16
 #pragma unroll
         for (int mt = 0; mt < kMT; ++mt) {
             const int m = mb + 16 * mt + r16;
             if (mt >= ntile || m >= n_e) continue;
-#pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                const int n = n0 + 16 * r + (lane >> 4) * 4;
-                uint32_t lo = (uint32_t)f32_to_bf16(silu_mul(ag[mt][r][0], au[mt][r][0])) |
-                              ((uint32_t)f32_to_bf16(silu_mul(ag[mt][r][1], au[mt][r][1])) << 16);
-                uint32_t hi = (uint32_t)f32_to_bf16(silu_mul(ag[mt][r][2], au[mt][r][2])) |
-                              ((uint32_t)f32_to_bf16(silu_mul(ag[mt][r][3], au[mt][r][3])) << 16);
-                *reinterpret_cast<uint2*>(h + (size_t)(beg + m) * I + n) = make_uint2(lo, hi);
-            }
+            const int n = n0 + (lane >> 4) * 4;
+            const f32x4 gv = g[mt][0], uv = u[mt][0];
+            uint32_t lo = (uint32_t)f32_to_bf16(silu_mul(gv[0], uv[0])) |
+                          ((uint32_t)f32_to_bf16(silu_mul(gv[1], uv[1])) << 16);
+            uint32_t hi = (uint32_t)f32_to_bf16(silu_mul(gv[2], uv[2])) |
+                          ((uint32_t)f32_to_bf16(silu_mul(gv[3], uv[3])) << 16);
+            *reinterpret_cast<uint2*>(h + (size_t)(beg + m) * I + n) = make_uint2(lo, hi);
         }
     }
 }
 
 // y_perm[beg+m, c] = w_pair * (h[beg+m] . Wd[e,c]) for the tokens m of expert e.
-// grid: (ceil(d / 128), E).
+// grid: (ceil(d / 64), E); block: 4 waves, each streaming 16 rows of Wd.
 __global__ __launch_bounds__(256) void down_stream_kernel(const u16* __restrict__ h,
                                                           const int32_t* __restrict__ offsets,
                                                           const int32_t* __restrict__ sorted_pairs,
@@ -104,42 +165,27 @@ __global__ __launch_bounds__(256) void down_stream_kernel(const u16* __restrict_
     const int n_e = offsets[e + 1] - beg;
     if (n_e <= 0) return;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int n0 = (blockIdx.x * kWavesPerBlock + wave) * kChanPerWave;
+    const int n0 = (blockIdx.x * kWavesPerBlock + wave) * 16;
     if (n0 >= d) return;
     const int r16 = lane & 15, kq = (lane >> 4) * 8;
-    const u16* w0 = Wd + ((size_t)e * d + n0 + r16) * I + kq;
-    const u16* w1 = w0 + (size_t)16 * I;
+    const u16* const a[1] = {Wd + ((size_t)e * d + n0 + r16) * I + kq};
     for (int mb = 0; mb < n_e; mb += 16 * kMT) {
         const int ntile = min(kMT, (n_e - mb + 15) / 16);
         const u16* hp[kMT];
 #pragma unroll
         for (int mt = 0; mt < kMT; ++mt) hp[mt] = h + (size_t)(beg + min(mb + 16 * mt + r16, n_e - 1)) * I + kq;
-        f32x4 acc[kMT][2];
-#pragma unroll
-        for (int mt = 0; mt < kMT; ++mt) { acc[mt][0] = f32x4{0, 0, 0, 0}; acc[mt][1] = f32x4{0, 0, 0, 0}; }
-#pragma unroll 2
-        for (int k = 0; k < I; k += 32) {
-            const bf16x8 a0 = ld8(w0 + k), a1 = ld8(w1 + k);
-#pragma unroll
-            for (int mt = 0; mt < kMT; ++mt) {
-                if (mt < ntile) {
-                    const bf16x8 hb = ld8(hp[mt] + k);
-                    acc[mt][0] = mfma16(a0, hb, acc[mt][0]);
-                    acc[mt][1] = mfma16(a1, hb, acc[mt][1]);
-                }
-            }
-        }
+        f32x4 acc[kMT][1];
+        zero_acc<kMT>(acc);
+        stream_core<1, kMT, kDdn, kNT>(a, hp, I, acc);
 #pragma unroll
         for (int mt = 0; mt < kMT; ++mt) {
             const int m = mb + 16 * mt + r16;
             if (mt >= ntile || m >= n_e) continue;
             const float wt = topk_w[sorted_pairs[beg + m]];
-#pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                const int c = n0 + 16 * r + (lane >> 4) * 4;
-                float4 v = make_float4(wt * acc[mt][r][0], wt * acc[mt][r][1], wt * acc[mt][r][2], wt * acc[mt][r][3]);
-                *reinterpret_cast<float4*>(y_perm + (size_t)(beg + m) * d + c) = v;
-            }
+            const int c = n0 + (lane >> 4) * 4;
+            const f32x4 v = acc[mt][0];
+            *reinterpret_cast<float4*>(y_perm + (size_t)(beg + m) * d + c) =
+                make_float4(wt * v[0], wt * v[1], wt * v[2], wt * v[3]);
         }
     }
 }
@@ -164,12 +210,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 }  // namespace
 
-int experts_tile_m(const Shape&) { return 64; }
+int experts_tile_m(const Shape&) { return 16 * kMT; }
 
 void launch_swiglu(const Shape& s, const void* x, const int32_t* offsets, const int32_t* sorted_pairs,
                    const int32_t* /*tiles*/, const int32_t* /*n_tiles*/, const void* Wg, const void* Wu, void* h,
                    hipStream_t st) {
-    const int per_block = kWavesPerBlock * kChanPerWave;
+    const int per_block = kWavesPerBlock * 16;
     hipLaunchKernelGGL(swiglu_stream_kernel, dim3((unsigned)((s.I + per_block - 1) / per_block), (unsigned)s.E),
                        dim3(256), 0, st, (const u16*)x, offsets, sorted_pairs, s.K, (const u16*)Wg, (const u16*)Wu,
                        (u16*)h, s.d, s.I);
@@ -178,7 +224,7 @@ void launch_swiglu(const Shape& s, const void* x, const int32_t* offsets, const 
 void launch_down(const Shape& s, const void* h, const int32_t* offsets, const int32_t* sorted_pairs,
                  const float* topk_w, const int32_t* /*tiles*/, const int32_t* /*n_tiles*/, const void* Wd,
                  float* y_perm, hipStream_t st) {
-    const int per_block = kWavesPerBlock * kChanPerWave;
+    const int per_block = kWavesPerBlock * 16;
     hipLaunchKernelGGL(down_stream_kernel, dim3((unsigned)((s.d + per_block - 1) / per_block), (unsigned)s.E),
                        dim3(256), 0, st, (const u16*)h, offsets, sorted_pairs, topk_w, (const u16*)Wd, y_perm, s.d,
                        s.I);
