@@ -61,7 +61,7 @@ Layout layout(const Shape& s) {
     L.off = o; o += up(((size_t)s.E + 1) * 4);
     L.sp = o; o += up(P * 4);
     L.pr = o; o += up(P * 4);
-    L.tiles = o; o += up(max_tiles * 2 * 4);
+    L.tiles = o; o += up(max_tiles * 4 * 4);
     L.ntiles = o; o += up(4);
     L.h = o; o += up(P * s.I * 2);
     L.yp = o; o += up(P * s.d * 4);

@@ -37,8 +37,9 @@ __device__ int block_excl_scan(int* buf, int* tmp, int n) {
     return total;
 }
 
-// Work tiles for the grouped GEMMs: (expert, first row) for every tile_m rows of each
-// expert's segment, expert-major. cnt[] holds per-expert counts on entry (clobbered).
+// Work tiles for the grouped GEMMs, expert-major: for every tile_m rows of each expert's
+// segment a record {expert, first row, index of the expert's first tile, tiles of the
+// expert}. cnt[] holds per-expert counts on entry (clobbered).
 __device__ void write_tiles(int* cnt, int* tmp, int E, int tile_m, int32_t* tiles, int32_t* n_tiles) {
     const int t = threadIdx.x;
     int mt = 0;
@@ -50,8 +51,11 @@ __device__ void write_tiles(int* cnt, int* tmp, int E, int tile_m, int32_t* tile
     const int total = block_excl_scan(cnt, tmp, E);
     if (t < E)
         for (int i = 0; i < mt; ++i) {
-            tiles[2 * (cnt[t] + i)] = t;
-            tiles[2 * (cnt[t] + i) + 1] = i * tile_m;
+            int32_t* rec = tiles + 4 * (cnt[t] + i);
+            rec[0] = t;
+            rec[1] = i * tile_m;
+            rec[2] = cnt[t];
+            rec[3] = mt;
         }
     if (t == 0) *n_tiles = total;
 }

@@ -210,11 +210,20 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 }  // namespace
 
-int experts_tile_m(const Shape&) { return 16 * kMT; }
+// Path choice from the average number of tokens per expert: up to 16 the weight-streaming
+// kernels (each expert's weights read once per 16 of its tokens), above that the tiled
+// grouped GEMM (weights read about once per call, tokens re-read from L2).
+bool experts_tiled(const Shape& s) { return gemm_supports(s) && s.T * (int64_t)s.K > 16 * (int64_t)s.E; }
+
+int experts_tile_m(const Shape& s) { return experts_tiled(s) ? gemm_tile_m() : 16 * kMT; }
 
 void launch_swiglu(const Shape& s, const void* x, const int32_t* offsets, const int32_t* sorted_pairs,
-                   const int32_t* /*tiles*/, const int32_t* /*n_tiles*/, const void* Wg, const void* Wu, void* h,
+                   const int32_t* tiles, const int32_t* n_tiles, const void* Wg, const void* Wu, void* h,
                    hipStream_t st) {
+    if (experts_tiled(s)) {
+        launch_gemm_swiglu(s, x, offsets, sorted_pairs, tiles, n_tiles, Wg, Wu, h, st);
+        return;
+    }
     const int per_block = kWavesPerBlock * 16;
     hipLaunchKernelGGL(swiglu_stream_kernel, dim3((unsigned)((s.I + per_block - 1) / per_block), (unsigned)s.E),
                        dim3(256), 0, st, (const u16*)x, offsets, sorted_pairs, s.K, (const u16*)Wg, (const u16*)Wu,
@@ -222,8 +231,12 @@ void launch_swiglu(const Shape& s, const void* x, const int32_t* offsets, const 
 }
 
 void launch_down(const Shape& s, const void* h, const int32_t* offsets, const int32_t* sorted_pairs,
-                 const float* topk_w, const int32_t* /*tiles*/, const int32_t* /*n_tiles*/, const void* Wd,
+                 const float* topk_w, const int32_t* tiles, const int32_t* n_tiles, const void* Wd,
                  float* y_perm, hipStream_t st) {
+    if (experts_tiled(s)) {
+        launch_gemm_down(s, h, offsets, sorted_pairs, topk_w, tiles, n_tiles, Wd, y_perm, st);
+        return;
+    }
     const int per_block = kWavesPerBlock * 16;
     hipLaunchKernelGGL(down_stream_kernel, dim3((unsigned)((s.d + per_block - 1) / per_block), (unsigned)s.E),
                        dim3(256), 0, st, (const u16*)h, offsets, sorted_pairs, topk_w, (const u16*)Wd, y_perm, s.d,

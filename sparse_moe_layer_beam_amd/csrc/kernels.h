@@ -27,8 +27,17 @@ void launch_dispatch(const Shape& s, const int32_t* idx, int32_t* offsets, int32
                      int32_t* pair_rank, int32_t* chunk_counts, int32_t* rank_in_chunk, int32_t* tiles,
                      int32_t* n_tiles, int tile_m, hipStream_t st);
 
-// Experts (experts.hip)
+// Experts (experts.hip: path choice, streaming kernels, combine; grouped_gemm.hip: tiled GEMM)
 int experts_tile_m(const Shape& s);
+bool experts_tiled(const Shape& s);
+int gemm_tile_m();
+bool gemm_supports(const Shape& s);
+void launch_gemm_swiglu(const Shape& s, const void* x, const int32_t* offsets, const int32_t* sorted_pairs,
+                        const int32_t* tiles, const int32_t* n_tiles, const void* Wg, const void* Wu, void* h,
+                        hipStream_t st);
+void launch_gemm_down(const Shape& s, const void* h, const int32_t* offsets, const int32_t* sorted_pairs,
+                      const float* topk_w, const int32_t* tiles, const int32_t* n_tiles, const void* Wd,
+                      float* y_perm, hipStream_t st);
 void launch_swiglu(const Shape& s, const void* x, const int32_t* offsets, const int32_t* sorted_pairs,
                    const int32_t* tiles, const int32_t* n_tiles, const void* Wg, const void* Wu, void* h,
                    hipStream_t st);
