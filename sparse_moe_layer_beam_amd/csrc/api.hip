@@ -43,7 +43,7 @@ size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 // Workspace segments, each 256-byte aligned.
 struct Layout {
-    size_t xn, zp, idx, w, cc, ric, off, sp, pr, tiles, ntiles, h, yp, total;
+    size_t xn, wrs, zp, idx, w, cc, ric, off, sp, pr, tiles, ntiles, h, yp, total;
 };
 
 Layout layout(const Shape& s) {
@@ -53,6 +53,7 @@ Layout layout(const Shape& s) {
     Layout L{};
     size_t o = 0;
     L.xn = o; o += up(T * s.d * 2);
+    L.wrs = o; o += up(beam::router_split_bytes(s));
     L.zp = o; o += up((size_t)beam::router_ksplit(s) * T * s.E * 4);
     L.idx = o; o += up(P * 4);
     L.w = o; o += up(P * 4);
@@ -82,10 +83,7 @@ void run_route(const Shape& s, const Layout& L, const void* x, const void* norm_
         beam::launch_rmsnorm(s, x, norm_w, x_normed, st);
         xin = x_normed;
     }
-    const int ks = beam::router_ksplit(s);
-    float* zp = at<float>(ws, L.zp);
-    beam::launch_router_logits(s, xin, Wr, zp, ks, st);
-    beam::launch_router_topk(s, zp, ks, bias, idx, w, logits, st);
+    beam::launch_router(s, xin, Wr, bias, at<void>(ws, L.wrs), at<float>(ws, L.zp), idx, w, logits, st);
 }
 
 }  // namespace

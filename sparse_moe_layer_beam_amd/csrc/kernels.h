@@ -17,9 +17,11 @@ struct Shape {
 // Router (router.hip)
 void launch_rmsnorm(const Shape& s, const void* h, const void* w, void* x_out, hipStream_t st);
 int router_ksplit(const Shape& s);
-void launch_router_logits(const Shape& s, const void* x, const float* Wr, float* z_part, int ks, hipStream_t st);
-void launch_router_topk(const Shape& s, const float* z_part, int ks, const float* bias, int32_t* idx, float* w,
-                        float* logits, hipStream_t st);
+size_t router_split_bytes(const Shape& s);
+// Logits, sigmoid, bias, group-limited top-k and weights for T tokens (x already normed).
+// wrs: scratch of router_split_bytes(s); z_part: scratch of router_ksplit(s) * T * E floats.
+void launch_router(const Shape& s, const void* x, const float* Wr, const float* bias, void* wrs, float* z_part,
+                   int32_t* idx, float* w, float* logits, hipStream_t st);
 
 // Dispatch (dispatch.hip)
 constexpr int kChunkPairs = 1024;

@@ -122,17 +122,14 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const u16* __restric
 }
 
 // ---------------------------------------------------------------------------------------
-// Selection, one wavefront per token. Lane l holds experts [l*EPL, (l+1)*EPL); a group of
-// E/G experts spans LPG = E/(G*EPL) adjacent lanes (a power of two), so the group top-2
-// is an xor-butterfly inside aligned lane blocks. Ties go to the lower index everywhere.
+// Selection for one token, by one whole wavefront. Lane l holds the logits of experts
+// [l*EPL, (l+1)*EPL); a group of E/G experts spans LPG = E/(G*EPL) adjacent lanes (a power
+// of two), so the group top-2 is an xor-butterfly inside aligned lane blocks. Ties go to
+// the lower index everywhere. Writes idx/w rows (and the logits row when asked).
 template <int EPL>
-__global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ zp, int ks, int64_t T, int E,
-                                                          int G, int KG, int K, float S, int norm,
-                                                          const float* __restrict__ bias, int32_t* __restrict__ idx,
-                                                          float* __restrict__ wout, float* __restrict__ logits) {
-    const int lane = threadIdx.x & 63;
-    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= T) return;
+__device__ __forceinline__ void select_token(const float (&z)[EPL], int lane, int E, int G, int KG, int K, float S,
+                                             int norm, const float* __restrict__ bias, int32_t* __restrict__ idx_row,
+                                             float* __restrict__ w_row, float* __restrict__ logits_row) {
     const int e0 = lane * EPL;
     const bool live = e0 < E;
     const float NEG = -INFINITY;
@@ -143,10 +140,8 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
         s[i] = 0.0f;
         b[i] = NEG;
         if (e < E) {
-            float z = 0.0f;
-            for (int q = 0; q < ks; ++q) z += zp[((int64_t)q * T + t) * E + e];
-            if (logits) logits[t * E + e] = z;
-            s[i] = 1.0f / (1.0f + expf(-z));
+            if (logits_row) logits_row[e] = z[i];
+            s[i] = 1.0f / (1.0f + expf(-z[i]));
             b[i] = s[i] + bias[e];
         }
     }
@@ -201,8 +196,187 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
         if (lane == j) { my_e = e; my_s = se; }
     }
     if (lane < K) {
-        idx[t * K + lane] = my_e;
-        wout[t * K + lane] = norm ? S * my_s / sum : S * my_s;
+        idx_row[lane] = my_e;
+        w_row[lane] = norm ? S * my_s / sum : S * my_s;
+    }
+}
+
+// Selection from K-split partial logits zp [ks][T][E]: one wavefront per token; the ks
+// partial sums of each logit are added in ascending split order (deterministic).
+template <int EPL>
+__global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ zp, int ks, int64_t T, int E,
+                                                          int G, int KG, int K, float S, int norm,
+                                                          const float* __restrict__ bias, int32_t* __restrict__ idx,
+                                                          float* __restrict__ wout, float* __restrict__ logits) {
+    const int lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const int e0 = lane * EPL;
+    float z[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) z[i] = 0.0f;
+    if (e0 < E) {
+        if constexpr (EPL == 4) {
+            // E is a multiple of 64 here, so each lane's 4 logits are one aligned float4
+            int q = 0;
+            for (; q + 8 <= ks; q += 8) {
+                float4 v[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    v[u] = *reinterpret_cast<const float4*>(zp + ((int64_t)(q + u) * T + t) * E + e0);
+#pragma unroll
+                for (int u = 0; u < 8; ++u) { z[0] += v[u].x; z[1] += v[u].y; z[2] += v[u].z; z[3] += v[u].w; }
+            }
+            for (; q < ks; ++q) {
+                const float4 v = *reinterpret_cast<const float4*>(zp + ((int64_t)q * T + t) * E + e0);
+                z[0] += v.x; z[1] += v.y; z[2] += v.z; z[3] += v.w;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < EPL; ++i)
+                if (e0 + i < E)
+                    for (int q = 0; q < ks; ++q) z[i] += zp[((int64_t)q * T + t) * E + e0 + i];
+        }
+    }
+    select_token<EPL>(z, lane, E, G, KG, K, S, norm, bias, idx + t * K, wout + t * K, logits ? logits + t * E : nullptr);
+}
+
+// ---------------------------------------------------------------------------------------
+// Router GEMM on BF16 MFMA with FP32-exact products. Each FP32 router weight is split into
+// three bf16 parts (hi + mid + lo = w exactly: 8 + 8 + 8 significant bits); x is bf16 already,
+// so x*hi, x*mid and x*lo are exact and are accumulated in FP32 by the MFMA, the same FP32
+// dot product the vector path computes, about 10x faster.
+
+// Wr [d, E] fp32 -> WrS [3][E][d] bf16 (expert-major, k contiguous: the MFMA B-operand layout).
+__global__ __launch_bounds__(256) void router_split_kernel(const float* __restrict__ Wr, u16* __restrict__ WrS,
+                                                           int d, int E) {
+    __shared__ float tile[64][65];
+    const int k0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
+    for (int i = threadIdx.x; i < 64 * 16; i += 256) {
+        const int kk = i >> 4, ec = (i & 15) * 4;
+        const float4 v = *reinterpret_cast<const float4*>(Wr + (size_t)(k0 + kk) * E + e0 + ec);
+        tile[kk][ec] = v.x; tile[kk][ec + 1] = v.y; tile[kk][ec + 2] = v.z; tile[kk][ec + 3] = v.w;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < 64 * 8; i += 256) {
+        const int e = i >> 3, kc = (i & 7) * 8;
+        uint32_t p[3][4];
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+            uint32_t h2[3][2];
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                const float w = tile[kc + j + jj][e];
+                const float hi = __uint_as_float(__float_as_uint(w) & 0xffff0000u);
+                const float r1 = w - hi;
+                const float mid = __uint_as_float(__float_as_uint(r1) & 0xffff0000u);
+                const float r2 = r1 - mid;
+                h2[0][jj] = __float_as_uint(hi) >> 16;
+                h2[1][jj] = __float_as_uint(mid) >> 16;
+                h2[2][jj] = (uint32_t)f32_to_bf16(r2);
+            }
+#pragma unroll
+            for (int pl = 0; pl < 3; ++pl) p[pl][j / 2] = h2[pl][0] | (h2[pl][1] << 16);
+        }
+#pragma unroll
+        for (int pl = 0; pl < 3; ++pl)
+            *reinterpret_cast<uint4*>(WrS + ((size_t)pl * E + e0 + e) * d + k0 + kc) =
+                make_uint4(p[pl][0], p[pl][1], p[pl][2], p[pl][3]);
+    }
+}
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Block: 64 tokens x E experts (4 waves of E/4 experts = NTW tiles of 16), k range
+// [blockIdx.y*kc, +kc). FUSED (kc = d): logits go through LDS and the block selects the
+// experts of its 64 tokens. Otherwise the partial logits go to zp[blockIdx.y].
+template <int NTW, bool FUSED>
+__global__ __launch_bounds__(256, 2) void router_mfma_kernel(const u16* __restrict__ x, const u16* __restrict__ WrS,
+                                                             float* __restrict__ zp, int64_t T, int d, int E, int kc,
+                                                             int G, int KG, int K, float S, int norm,
+                                                             const float* __restrict__ bias,
+                                                             int32_t* __restrict__ idx, float* __restrict__ wout,
+                                                             float* __restrict__ logits) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t t0 = (int64_t)blockIdx.x * 64;
+    const int kb = blockIdx.y * kc;
+    const int kq = (lane >> 4) * 8;
+    const u16* ap[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t t = min(t0 + 16 * i + (lane & 15), T - 1);   // rows past the end repeat; not stored
+        ap[i] = x + t * d + kb + kq;
+    }
+    const int ew = wave * (NTW * 16);
+    const u16* bp[NTW][3];
+#pragma unroll
+    for (int j = 0; j < NTW; ++j)
+#pragma unroll
+        for (int pl = 0; pl < 3; ++pl) bp[j][pl] = WrS + ((size_t)pl * E + ew + 16 * j + (lane & 15)) * d + kb + kq;
+    f32x4 acc[4][NTW];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
+    bf16x8 a[2][4], bw[2][NTW][3];
+    auto load = [&](int buf, int k) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[buf][i] = *reinterpret_cast<const bf16x8*>(ap[i] + k);
+#pragma unroll
+        for (int j = 0; j < NTW; ++j)
+#pragma unroll
+            for (int pl = 0; pl < 3; ++pl) bw[buf][j][pl] = *reinterpret_cast<const bf16x8*>(bp[j][pl] + k);
+    };
+    auto mma = [&](int buf) {
+#pragma unroll
+        for (int pl = 0; pl < 3; ++pl)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < NTW; ++j) acc[i][j] = mfma16(a[buf][i], bw[buf][j][pl], acc[i][j]);
+    };
+    // two k-steps in flight; kc is a multiple of 64
+    load(0, 0);
+    for (int k = 0; k < kc; k += 64) {
+        load(1, min(k + 32, kc - 32));
+        mma(0);
+        load(0, min(k + 64, kc - 32));
+        mma(1);
+    }
+    // acc[i][j][v]: token 16*i + 4*(lane/16) + v, expert ew + 16*j + lane%16
+    if constexpr (!FUSED) {
+        float* out = zp + (size_t)blockIdx.y * T * E;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int64_t t = t0 + 16 * i + 4 * (lane >> 4) + v;
+                if (t >= T) continue;
+#pragma unroll
+                for (int j = 0; j < NTW; ++j) out[t * E + ew + 16 * j + (lane & 15)] = acc[i][j][v];
+            }
+    } else {
+        __shared__ float zs[64][NTW * 64 + 4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+#pragma unroll
+                for (int j = 0; j < NTW; ++j) zs[16 * i + 4 * (lane >> 4) + v][ew + 16 * j + (lane & 15)] = acc[i][j][v];
+        __syncthreads();
+        constexpr int EPL = NTW;   // E = 64 * NTW: NTW logits per lane
+        for (int r = wave; r < 64; r += 4) {
+            const int64_t t = t0 + r;
+            if (t >= T) break;
+            float z[EPL];
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) z[i] = zs[r][lane * EPL + i];
+            select_token<EPL>(z, lane, E, G, KG, K, S, norm, bias, idx + t * K, wout + t * K,
+                              logits ? logits + t * E : nullptr);
+        }
     }
 }
 
@@ -213,8 +387,22 @@ void launch_rmsnorm(const Shape& s, const void* h, const void* w, void* x_out, h
                        (u16*)x_out, s.d, (double)s.eps);
 }
 
+bool router_uses_mfma(const Shape& s) { return (s.E == 128 || s.E == 256) && s.d % 64 == 0; }
+
+// Blocks of 64 tokens; batches of 1024+ blocks run the fused full-K kernel, smaller ones split
+// K so that about 1024 blocks share the work (and the 5 MB router weight).
 int router_ksplit(const Shape& s) {
-    const int64_t tiles = (int64_t)((s.E + RE - 1) / RE) * ((s.T + RT - 1) / RT);
+    const int64_t tb = (s.T + 63) / 64;
+    if (router_uses_mfma(s)) {
+        if (tb >= 1024) return 1;                   // enough blocks for the fused full-K kernel
+        const int steps = s.d / 64;                 // 64-wide k chunks
+        int want = (int)(1024 / tb);
+        int ks = 1;
+        for (int c = 1; c <= want && c <= 64; ++c)
+            if (steps % c == 0 && steps / c >= 2) ks = c;
+        return ks;
+    }
+    const int64_t tiles = (int64_t)((s.E + RE - 1) / RE) * tb;
     int64_t want = 512 / (tiles > 0 ? tiles : 1);
     if (want < 1) want = 1;
     if (want > 16) want = 16;
@@ -225,18 +413,34 @@ int router_ksplit(const Shape& s) {
     return ks;
 }
 
-void launch_router_logits(const Shape& s, const void* x, const float* Wr, float* z_part, int ks, hipStream_t st) {
-    dim3 grid((unsigned)((s.T + RT - 1) / RT), (unsigned)((s.E + RE - 1) / RE), (unsigned)ks);
-    hipLaunchKernelGGL(router_logits_kernel, grid, dim3(256), 0, st, (const u16*)x, Wr, z_part, s.T, s.d, s.E,
-                       s.d / ks);
-}
+size_t router_split_bytes(const Shape& s) { return router_uses_mfma(s) ? (size_t)3 * s.E * s.d * 2 : 0; }
 
-void launch_router_topk(const Shape& s, const float* z_part, int ks, const float* bias, int32_t* idx, float* w,
-                        float* logits, hipStream_t st) {
-    dim3 grid((unsigned)((s.T + 3) / 4));
+void launch_router(const Shape& s, const void* x, const float* Wr, const float* bias, void* wrs, float* z_part,
+                   int32_t* idx, float* w, float* logits, hipStream_t st) {
+    const int ks = router_ksplit(s);
     const int epl = s.E <= 64 ? 1 : s.E / 64;
+    const unsigned tb = (unsigned)((s.T + 63) / 64);
+    if (router_uses_mfma(s)) {
+        hipLaunchKernelGGL(router_split_kernel, dim3((unsigned)(s.d / 64), (unsigned)(s.E / 64)), dim3(256), 0, st,
+                           Wr, (u16*)wrs, s.d, s.E);
+#define BEAM_RMMA(NTW, F)                                                                                        \
+    hipLaunchKernelGGL((router_mfma_kernel<NTW, F>), dim3(tb, (unsigned)ks), dim3(256), 0, st, (const u16*)x,     \
+                       (const u16*)wrs, z_part, s.T, s.d, s.E, s.d / ks, s.G, s.KG, s.K, s.S, s.norm, bias, idx, w, \
+                       logits)
+        if (ks == 1) {
+            if (s.E == 256) BEAM_RMMA(4, true); else BEAM_RMMA(2, true);
+            return;
+        }
+        if (s.E == 256) BEAM_RMMA(4, false); else BEAM_RMMA(2, false);
+#undef BEAM_RMMA
+    } else {
+        dim3 grid(tb, (unsigned)((s.E + RE - 1) / RE), (unsigned)ks);
+        hipLaunchKernelGGL(router_logits_kernel, grid, dim3(256), 0, st, (const u16*)x, Wr, z_part, s.T, s.d, s.E,
+                           s.d / ks);
+    }
+    dim3 grid((unsigned)((s.T + 3) / 4));
 #define BEAM_TOPK(N)                                                                                              \
-    hipLaunchKernelGGL(router_topk_kernel<N>, grid, dim3(256), 0, st, z_part, ks, s.T, s.E, s.G, s.KG, s.K, s.S, \
+    hipLaunchKernelGGL(router_topk_kernel<N>, grid, dim3(256), 0, st, z_part, ks, s.T, s.E, s.G, s.KG, s.K, s.S,  \
                        s.norm, bias, idx, w, logits)
     switch (epl) {
         case 1: BEAM_TOPK(1); break;
