@@ -191,21 +191,25 @@ __global__ __launch_bounds__(256) void down_stream_kernel(const u16* __restrict_
 }
 
 // y[t] = sum over slots j = 0..K-1, in that order, of y_perm[pair_rank[t*K + j]].
+// grid: (T, ceil(d / 1024)); each thread owns one float4 of the row.
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y_perm,
                                                       const int32_t* __restrict__ pair_rank, int K, int d,
                                                       float* __restrict__ y) {
     const int64_t t = blockIdx.x;
-    __shared__ int rk[16];
-    if (threadIdx.x < K) rk[threadIdx.x] = pair_rank[t * K + threadIdx.x];
-    __syncthreads();
-    for (int c = threadIdx.x * 4; c < d; c += 256 * 4) {
-        float4 acc = *reinterpret_cast<const float4*>(y_perm + (size_t)rk[0] * d + c);
-        for (int j = 1; j < K; ++j) {
-            const float4 v = *reinterpret_cast<const float4*>(y_perm + (size_t)rk[j] * d + c);
-            acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
-        }
-        *reinterpret_cast<float4*>(y + t * d + c) = acc;
-    }
+    const int c = (blockIdx.y * 256 + threadIdx.x) * 4;
+    if (c >= d) return;
+    int rk[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) rk[j] = j < K ? pair_rank[t * K + j] : 0;
+    float4 v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+        if (j < K) v[j] = *reinterpret_cast<const float4*>(y_perm + (size_t)rk[j] * d + c);
+    float4 acc = v[0];
+#pragma unroll
+    for (int j = 1; j < 16; ++j)
+        if (j < K) { acc.x += v[j].x; acc.y += v[j].y; acc.z += v[j].z; acc.w += v[j].w; }
+    *reinterpret_cast<float4*>(y + t * d + c) = acc;
 }
 
 }  // namespace
@@ -244,7 +248,8 @@ void launch_down(const Shape& s, const void* h, const int32_t* offsets, const in
 }
 
 void launch_combine(const Shape& s, const float* y_perm, const int32_t* pair_rank, float* y, hipStream_t st) {
-    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)s.T), dim3(256), 0, st, y_perm, pair_rank, s.K, s.d, y);
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)s.T, (unsigned)((s.d + 1023) / 1024)), dim3(256), 0, st, y_perm,
+                       pair_rank, s.K, s.d, y);
 }
 
 }  // namespace beam
