@@ -44,6 +44,10 @@ def lib():
         L.oracle_dispatch.argtypes = [vp, i64, i32, vp, vp, vp]
         L.oracle_expert.argtypes = [vp, i64, vp, vp, vp, i32, i32, vp, i32]
         L.oracle_moe_rows.argtypes = [vp, i64, vp, vp, i32, vp, vp, vp, i32, i32, vp, i32]
+        L.oracle_post_norm.argtypes = [vp, vp, i64, i32, dbl, vp, i32]
+        L.oracle_residual_step.argtypes = [vp, vp, i64, i32, vp]
+        L.oracle_contribution_index.argtypes = [i32, i32]
+        L.oracle_contribution_index.restype = i32
         _lib = L
     return _lib
 
@@ -164,3 +168,34 @@ def forward(x, Wr, bias, Wg, Wu, Wd, n_group, topk_group, top_k, scale, norm_top
     experts = {e: (Wg[e], Wu[e], Wd[e]) for e in range(E)}
     y = moe_rows(x, idx, w, experts, E)
     return y, idx, w, gap
+
+
+def post_norm(y: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
+    """Post-MLP RMSNorm of y [T,d] (any float, taken as double), w [d] bf16 bits -> [T,d] float64."""
+    y = _c(y, np.float64)
+    w = _c(w, np.uint16)
+    T, d = y.shape
+    n = np.empty_like(y)
+    lib().oracle_post_norm(y.ctypes.data, w.ctypes.data, T, d, float(eps), n.ctypes.data, nthreads())
+    return n
+
+
+def residual_step(r: np.ndarray, c: np.ndarray, k: int) -> np.ndarray:
+    """Stream after adding the k-th contribution c: r*sqrt((k-1)/k) + c/sqrt(k), float64."""
+    r = _c(r, np.float64)
+    c = _c(c, np.float64)
+    if r.shape != c.shape:
+        raise ValueError("shape mismatch")
+    out = np.empty_like(r)
+    lib().oracle_residual_step(r.ctypes.data, c.ctypes.data, r.size, int(k), out.ctypes.data)
+    return out
+
+
+def contribution_index(layer: int, is_mlp: bool) -> int:
+    return int(lib().oracle_contribution_index(int(layer), int(bool(is_mlp))))
+
+
+def post_residual(y, w, eps, resid, layer):
+    """MoE output y [T,d] -> residual stream after the MLP of 0-indexed layer `layer` (float64)."""
+    k = contribution_index(layer, True)
+    return residual_step(resid, post_norm(y, w, eps), k)

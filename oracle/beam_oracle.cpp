@@ -25,6 +25,13 @@
 //      archdb fact sheet, FFN rows];
 //   * y = sum of the weighted expert outputs, no shared expert [archdb fact sheet,
 //     MoE: always-on experts = 0].
+//   * after the layer (next step on the path, optional): the post-MLP half of the
+//     sandwich norm on y, then the depth-scaled residual add, the k-th contribution
+//     entering as r * sqrt((k-1)/k) + n / sqrt(k), where the embedding counts as the
+//     first contribution and the MLP of 0-indexed layer i as contribution 2(i+1)+1
+//     [Transformers "Beam" page, Overview: sandwich norms item; archdb fact sheet,
+//      normalisation and residual rows; news.hamidun.com article, section on hybrid
+//      attention and the unusual residual stream].
 //
 // Readings taken where the pages leave a step open:
 //   - the bias selects only: group scores and the top-k use b, the weights use s;
@@ -33,6 +40,8 @@
 //   - the SwiGLU output h is rounded to bf16 once before the down projection
 //     (the down projection is a bf16 GEMM); y is reported without rounding;
 //   - the RMSNorm output is rounded to bf16 once, x = bf16((h * r) * w).
+//   - the post-MLP RMSNorm reads the unrounded y and is not rounded either: the
+//     residual stream it feeds is accumulated in FP32 (archdb fact sheet, residual row).
 //
 // Layouts (row-major): x [T,d] bf16 bits, Wr [d,E] fp32, bias [E] fp32,
 // Wg[e], Wu[e] [I,d] bf16 bits (one row per intermediate channel), Wd[e] [d,I].
@@ -269,5 +278,33 @@ void oracle_moe_rows(const uint16_t* x_rows, int64_t n, const int32_t* idx, cons
             y_out[i * d + c] = acc;
         }
 }
+
+
+// Post-MLP RMSNorm of the layer output y [T,d] (double, unrounded): n[t,j] = y[t,j] * r_t * w[j],
+// r_t = 1 / sqrt(mean_j y[t,j]^2 + eps).
+void oracle_post_norm(const double* y, const uint16_t* w, int64_t T, int32_t d, double eps, double* n_out,
+                      int32_t nthreads) {
+    parallel_for(T, nthreads, [&](int64_t t) {
+        const double* yr = y + t * d;
+        double ss = 0.0;
+        for (int j = 0; j < d; ++j) ss += yr[j] * yr[j];
+        double r = 1.0 / std::sqrt(ss / d + eps);
+        for (int j = 0; j < d; ++j) n_out[t * d + j] = yr[j] * r * bf16_value(w[j]);
+    });
+}
+
+// Depth-scaled residual add of the k-th contribution c to the stream r (k >= 1):
+// r_out = r * sqrt((k-1)/k) + c / sqrt(k). After contributions c_1..c_m added with
+// k = 1..m the stream is (c_1 + ... + c_m) / sqrt(m).
+void oracle_residual_step(const double* r, const double* c, int64_t n, int32_t k, double* r_out) {
+    const double keep = std::sqrt((double)(k - 1) / (double)k);
+    const double add = 1.0 / std::sqrt((double)k);
+    for (int64_t i = 0; i < n; ++i) r_out[i] = r[i] * keep + c[i] * add;
+}
+
+// Position of a sublayer's output among the residual contributions: the embedding is the
+// first, then attention and MLP of each layer in turn (0-indexed layer i: attention 2(i+1),
+// MLP 2(i+1)+1).
+int32_t oracle_contribution_index(int32_t layer, int32_t is_mlp) { return 2 * (layer + 1) + (is_mlp ? 1 : 0); }
 
 }  // extern "C"

@@ -13,7 +13,7 @@ import subprocess
 import numpy as np
 
 from .recipes import (WORKLOADS, Workload, TID_X, TID_WR, TID_BIAS, TID_WG, TID_WU, TID_WD,
-                      TID_H, TID_NORMW, TID_HOT)
+                      TID_H, TID_NORMW, TID_HOT, TID_RESID, TID_POSTW)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 HOST_LIB = os.path.join(_HERE, "libsynth_host.so")
@@ -157,6 +157,17 @@ def hidden(w: Workload, rows=None) -> np.ndarray:
 def norm_weight(w: Workload) -> np.ndarray:
     """Pre-MLP RMSNorm weight, [d] bf16 bits, N(1, 0.02)."""
     return host_normal(w.d, w.seed, TID_NORMW, 1.0, 0.02, BF16)
+
+
+def post_norm_weight(w: Workload) -> np.ndarray:
+    """Post-MLP RMSNorm weight, [d] bf16 bits, N(1, 0.02)."""
+    return host_normal(w.d, w.seed, TID_POSTW, 1.0, 0.02, BF16)
+
+
+def residual(w: Workload) -> np.ndarray:
+    """Residual stream before the MLP's contribution, [T, d] fp32, N(0, 1) (the depth-scaled
+    residual keeps the stream at unit scale)."""
+    return host_normal(w.T * w.d, w.seed, TID_RESID, 0.0, 1.0, F32).reshape(w.T, w.d)
 
 
 def expert_weights(w: Workload, e: int):

@@ -24,6 +24,8 @@ TID_WD = 6       # down projections, [E, d, I] bf16
 TID_H = 7        # pre-norm hidden states (large-chunk workload), [T, d] bf16
 TID_NORMW = 8    # pre-MLP RMSNorm weight, [d] bf16
 TID_HOT = 9      # permutation that picks the hot experts (skewed workload)
+TID_RESID = 10   # residual stream entering the post-MLP add, [T, d] fp32
+TID_POSTW = 11   # post-MLP RMSNorm weight, [d] bf16
 
 
 @dataclass(frozen=True)

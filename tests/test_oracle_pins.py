@@ -315,3 +315,68 @@ def test_rmsnorm_matches_torch_float64():
     xc = _ref.bf16_bits_to_f64(oracle.rmsnorm(c, nw, w.eps))[0]
     exp = _ref.bf16_bits_to_f64(_ref.f64_to_bf16_bits_rne(_ref.bf16_bits_to_f64(nw) / math.sqrt(1 + w.eps)))
     assert np.array_equal(xc, exp)
+
+
+# --- post-MLP norm and depth-scaled residual ------------------------------------------------
+
+def test_residual_step_telescopes_to_sum_over_sqrt_k():
+    """After contributions c_1..c_m the stream is their sum over sqrt(m), the property the
+    Beam page states for the depth-scaled residual. A wrong k offset, a swapped keep/add
+    factor or a missing square root breaks it."""
+    rng = np.random.default_rng(7)
+    m, n = 12, 257
+    cs = rng.standard_normal((m, n))
+    r = rng.standard_normal(n) * 1e3            # k = 1 keeps nothing of what came before
+    for k in range(1, m + 1):
+        r = oracle.residual_step(r, cs[k - 1], k)
+        np.testing.assert_allclose(r, cs[:k].sum(0) / math.sqrt(k), rtol=1e-13, atol=1e-13)
+
+
+def test_residual_schedule_over_the_whole_model():
+    """Embedding first, then attention and MLP of each layer: the contribution indices run
+    2, 3, ..., 105 without a gap, there are as many additions as the pages print, and at the
+    end every contribution weighs the same (sum of squared weights 1)."""
+    g = json.load(open(os.path.join(GOLDEN, "beam_shape_facts.json")))
+    L = g["num_hidden_layers"]["value"]
+    ks = []
+    for i in range(L):
+        ks += [oracle.contribution_index(i, False), oracle.contribution_index(i, True)]
+    assert ks == list(range(2, 2 * L + 2))
+    assert len(ks) == g["residual_additions"]["value"]
+    n = len(ks) + 1
+    eye = np.eye(n)
+    r = oracle.residual_step(np.zeros(n), eye[0], 1)      # the embedding
+    for j, k in enumerate(ks):
+        r = oracle.residual_step(r, eye[j + 1], k)
+    np.testing.assert_allclose(r, np.full(n, 1 / math.sqrt(n)), rtol=1e-13)
+    assert abs((r ** 2).sum() - 1.0) < 1e-13
+    # the MoE layers are MLP sublayers: layer i enters as contribution 2(i+1)+1
+    assert [oracle.contribution_index(i, True) for i in (0, 3, 51)] == [3, 9, 105]
+
+
+def test_post_norm_closed_forms_and_torch():
+    """RMSNorm of the FP32 layer output: constant and one-hot rows in closed form, exact
+    power-of-two scale invariance at eps = 0, and torch float64 on random rows. A sum in
+    place of the mean, eps outside the root or a dropped weight fails one of them."""
+    w = recipes.WORKLOADS[1]
+    nw = synth.norm_weight(w)
+    wv = _ref.bf16_bits_to_f64(nw)
+    d, eps = w.d, w.eps
+    c = np.full((1, d), 0.37)
+    np.testing.assert_allclose(oracle.post_norm(c, nw, eps)[0], 0.37 / math.sqrt(0.37 ** 2 + eps) * wv, rtol=1e-15)
+    oh = np.zeros((1, d)); oh[0, 11] = -3.0
+    n = oracle.post_norm(oh, nw, eps)[0]
+    assert np.count_nonzero(n) == 1
+    assert abs(n[11] - (-3.0 / math.sqrt(9.0 / d + eps)) * wv[11]) <= 1e-15 * abs(n[11])
+    rng = np.random.default_rng(3)
+    y = rng.standard_normal((9, d)) * 0.05
+    base = oracle.post_norm(y, nw, 0.0)
+    for s in (8.0, 0.25):
+        assert np.array_equal(oracle.post_norm(y * s, nw, 0.0), base)
+    ones = np.full(d, 0x3F80, dtype=np.uint16)
+    n1 = oracle.post_norm(y, ones, eps)
+    ms = (y ** 2).mean(1)
+    np.testing.assert_allclose((n1 ** 2).mean(1), ms / (ms + eps), rtol=1e-13)
+    yt = torch.from_numpy(y)
+    ref = yt * torch.rsqrt(yt.pow(2).mean(-1, keepdim=True) + eps) * torch.from_numpy(wv)
+    np.testing.assert_allclose(oracle.post_norm(y, nw, eps), ref.numpy(), rtol=1e-14, atol=0)
