@@ -126,6 +126,40 @@ beam_moe_status beam_moe_forward_staged(const beam_moe_shape* shape, const void*
                                         const void* Wd, float* y, int32_t* topk_idx, float* topk_w, float* logits,
                                         void* workspace, size_t ws_bytes, void* stream, void* const* stage_events);
 
+/* Post-MLP half of the sandwich norm and the depth-scaled residual add (Transformers
+ * "Beam" page, Overview: sandwich norms item and FP32 RMSNorm note; archdb fact sheet,
+ * normalisation and residual rows: k = 2(i+1)+1 for the MLP of 0-indexed layer i, FP32
+ * residual accumulation; news.hamidun.com article, section on the residual stream).
+ * For every token t, in FP32:
+ *   n[t]         = y[t] * (1 / sqrt(mean_j y[t,j]^2 + rms_eps)) * post_w
+ *   resid_out[t] = resid[t] * sqrt((k-1)/k) + n[t] / sqrt(k),   k = 2 * (layer + 1) + 1
+ *   shape      the layer's shape; only T, d and rms_eps are used (the rest is still validated)
+ *   y          [T, d] FP32: the MoE output (as beam_moe_forward writes it)
+ *   post_w     [d] bf16: the post-MLP RMSNorm weight
+ *   layer      0-indexed decoder layer (>= 0, else BEAM_MOE_ERR_INVALID_ARG)
+ *   resid      [T, d] FP32: the residual stream before this MLP's contribution
+ *   resid_out  [T, d] FP32 out; may be the same buffer as resid (in place), must not
+ *              otherwise overlap it
+ * d up to 16384 (else BEAM_MOE_ERR_UNSUPPORTED_SHAPE). No workspace. */
+beam_moe_status beam_moe_post_residual(const beam_moe_shape* shape, const float* y, const void* post_w, int32_t layer,
+                                       const float* resid, float* resid_out, void* stream);
+
+/* The whole layer with the post-MLP norm and residual add fused into the combine: the
+ * same routing and expert work as beam_moe_forward_staged, then for each token the
+ * slot-ordered sum y[t] feeds beam_moe_post_residual's formula in the same kernel, so y
+ * need not make a round trip through HBM.
+ *   post_w, layer, resid, resid_out: as for beam_moe_post_residual
+ *   y          [T, d] FP32 out or NULL: the MoE output before the norm, bitwise equal to
+ *              beam_moe_forward's y (NULL skips the write)
+ *   stage_events: as for beam_moe_forward_staged ([5] follows the fused combine), or NULL
+ * Other arguments as for beam_moe_forward. */
+beam_moe_status beam_moe_forward_residual(const beam_moe_shape* shape, const void* x, const void* norm_w,
+                                          const float* Wr, const float* bias, const void* Wg, const void* Wu,
+                                          const void* Wd, const void* post_w, int32_t layer, const float* resid,
+                                          float* resid_out, float* y, int32_t* topk_idx, float* topk_w,
+                                          float* logits, void* workspace, size_t ws_bytes, void* stream,
+                                          void* const* stage_events);
+
 /* Static, human-readable name of a status code. */
 const char* beam_moe_status_string(beam_moe_status status);
 

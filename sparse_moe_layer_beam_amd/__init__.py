@@ -20,7 +20,8 @@ BEAM_MOE_ERR_WORKSPACE_TOO_SMALL = 3
 BEAM_MOE_ERR_HIP = 4
 
 EXPORTED = ("beam_moe_workspace_bytes", "beam_moe_route", "beam_moe_dispatch", "beam_moe_forward",
-            "beam_moe_forward_staged", "beam_moe_status_string")
+            "beam_moe_forward_staged", "beam_moe_post_residual", "beam_moe_forward_residual",
+            "beam_moe_status_string")
 N_STAGE_EVENTS = 6
 
 
@@ -68,6 +69,11 @@ def lib() -> ctypes.CDLL:
         L.beam_moe_forward.restype = i32
         L.beam_moe_forward_staged.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
         L.beam_moe_forward_staged.restype = i32
+        L.beam_moe_post_residual.argtypes = [shp, vp, vp, i32, vp, vp, vp]
+        L.beam_moe_post_residual.restype = i32
+        L.beam_moe_forward_residual.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp,
+                                                vp, sz, vp, vp]
+        L.beam_moe_forward_residual.restype = i32
         L.beam_moe_status_string.argtypes = [i32]
         L.beam_moe_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -148,3 +154,24 @@ def beam_moe_forward_staged(shape, x, norm_w, Wr, bias, Wg, Wu, Wd, y, topk_idx,
                                        _ptr(Wu), _ptr(Wd), _ptr(y), _ptr(topk_idx), _ptr(topk_w), _ptr(logits),
                                        _ptr(workspace), _nbytes(workspace), _stream(stream), arr)
     return _check(st, "beam_moe_forward_staged") if check else st
+
+
+def _events(stage_events):
+    if stage_events is None:
+        return None
+    return (ctypes.c_void_p * N_STAGE_EVENTS)(*[e if e else None for e in stage_events])
+
+
+def beam_moe_post_residual(shape, y, post_w, layer, resid, resid_out, stream=None, check=True) -> int:
+    st = lib().beam_moe_post_residual(ctypes.byref(shape), _ptr(y), _ptr(post_w), int(layer), _ptr(resid),
+                                      _ptr(resid_out), _stream(stream))
+    return _check(st, "beam_moe_post_residual") if check else st
+
+
+def beam_moe_forward_residual(shape, x, norm_w, Wr, bias, Wg, Wu, Wd, post_w, layer, resid, resid_out, y, topk_idx,
+                              topk_w, logits, workspace, stage_events=None, stream=None, check=True) -> int:
+    st = lib().beam_moe_forward_residual(ctypes.byref(shape), _ptr(x), _ptr(norm_w), _ptr(Wr), _ptr(bias), _ptr(Wg),
+                                         _ptr(Wu), _ptr(Wd), _ptr(post_w), int(layer), _ptr(resid), _ptr(resid_out),
+                                         _ptr(y), _ptr(topk_idx), _ptr(topk_w), _ptr(logits), _ptr(workspace),
+                                         _nbytes(workspace), _stream(stream), _events(stage_events))
+    return _check(st, "beam_moe_forward_residual") if check else st

@@ -138,18 +138,34 @@ beam_moe_status beam_moe_dispatch(const beam_moe_shape* shape, const int32_t* to
 
 namespace {
 
+// Optional post-MLP norm + depth-scaled residual applied in the combine.
+struct Post {
+    const void* w = nullptr;
+    int layer = 0;
+    const float* resid = nullptr;
+    float* resid_out = nullptr;
+};
+
+beam_moe_status check_post(const Shape& s, const Post& p) {
+    if (!p.w || !p.resid || !p.resid_out || p.layer < 0) return BEAM_MOE_ERR_INVALID_ARG;
+    if (!aligned(p.w) || !aligned(p.resid) || !aligned(p.resid_out)) return BEAM_MOE_ERR_INVALID_ARG;
+    if (s.d > beam::kPostMaxD) return BEAM_MOE_ERR_UNSUPPORTED_SHAPE;
+    return BEAM_MOE_OK;
+}
+
 beam_moe_status forward_impl(const beam_moe_shape* shape, const void* x, const void* norm_w, const float* Wr,
                              const float* bias, const void* Wg, const void* Wu, const void* Wd, float* y,
                              int32_t* topk_idx, float* topk_w, float* logits, void* workspace, size_t ws_bytes,
-                             void* stream, void* const* events) {
+                             void* stream, void* const* events, const Post* post) {
     Shape s;
     beam_moe_status st = to_shape(shape, &s);
     if (st != BEAM_MOE_OK) return st;
-    if (!x || !Wr || !bias || !Wg || !Wu || !Wd || !y) return BEAM_MOE_ERR_INVALID_ARG;
-    if (!aligned(x) || !aligned(Wr) || !aligned(bias) || !aligned(Wg) || !aligned(Wu) || !aligned(Wd) || !aligned(y) ||
-        (norm_w && !aligned(norm_w)) || (topk_idx && !aligned(topk_idx)) || (topk_w && !aligned(topk_w)) ||
-        (logits && !aligned(logits)))
+    if (!x || !Wr || !bias || !Wg || !Wu || !Wd || (!y && !post)) return BEAM_MOE_ERR_INVALID_ARG;
+    if (!aligned(x) || !aligned(Wr) || !aligned(bias) || !aligned(Wg) || !aligned(Wu) || !aligned(Wd) ||
+        (y && !aligned(y)) || (norm_w && !aligned(norm_w)) || (topk_idx && !aligned(topk_idx)) ||
+        (topk_w && !aligned(topk_w)) || (logits && !aligned(logits)))
         return BEAM_MOE_ERR_INVALID_ARG;
+    if (post && (st = check_post(s, *post)) != BEAM_MOE_OK) return st;
     if (s.T == 0) return BEAM_MOE_OK;
     const Layout L = layout(s);
     if (!workspace || !aligned(workspace)) return BEAM_MOE_ERR_INVALID_ARG;
@@ -180,7 +196,10 @@ beam_moe_status forward_impl(const beam_moe_shape* shape, const void* x, const v
     mark(3);
     beam::launch_down(s, h, off, sp, w, tiles, ntiles, Wd, yp, hs);
     mark(4);
-    beam::launch_combine(s, yp, pr, y, hs);
+    if (post)
+        beam::launch_combine_post_residual(s, yp, pr, post->w, post->layer, post->resid, post->resid_out, y, hs);
+    else
+        beam::launch_combine(s, yp, pr, y, hs);
     mark(5);
     return hip_status();
 }
@@ -194,7 +213,7 @@ beam_moe_status beam_moe_forward(const beam_moe_shape* shape, const void* x, con
                                  int32_t* topk_idx, float* topk_w, float* logits, void* workspace, size_t ws_bytes,
                                  void* stream) {
     return forward_impl(shape, x, norm_w, Wr, bias, Wg, Wu, Wd, y, topk_idx, topk_w, logits, workspace, ws_bytes,
-                        stream, nullptr);
+                        stream, nullptr, nullptr);
 }
 
 beam_moe_status beam_moe_forward_staged(const beam_moe_shape* shape, const void* x, const void* norm_w,
@@ -202,7 +221,40 @@ beam_moe_status beam_moe_forward_staged(const beam_moe_shape* shape, const void*
                                         const void* Wd, float* y, int32_t* topk_idx, float* topk_w, float* logits,
                                         void* workspace, size_t ws_bytes, void* stream, void* const* stage_events) {
     return forward_impl(shape, x, norm_w, Wr, bias, Wg, Wu, Wd, y, topk_idx, topk_w, logits, workspace, ws_bytes,
-                        stream, stage_events);
+                        stream, stage_events, nullptr);
+}
+
+beam_moe_status beam_moe_forward_residual(const beam_moe_shape* shape, const void* x, const void* norm_w,
+                                          const float* Wr, const float* bias, const void* Wg, const void* Wu,
+                                          const void* Wd, const void* post_w, int32_t layer, const float* resid,
+                                          float* resid_out, float* y, int32_t* topk_idx, float* topk_w,
+                                          float* logits, void* workspace, size_t ws_bytes, void* stream,
+                                          void* const* stage_events) {
+    Post p;
+    p.w = post_w;
+    p.layer = layer;
+    p.resid = resid;
+    p.resid_out = resid_out;
+    return forward_impl(shape, x, norm_w, Wr, bias, Wg, Wu, Wd, y, topk_idx, topk_w, logits, workspace, ws_bytes,
+                        stream, stage_events, &p);
+}
+
+beam_moe_status beam_moe_post_residual(const beam_moe_shape* shape, const float* y, const void* post_w, int32_t layer,
+                                       const float* resid, float* resid_out, void* stream) {
+    Shape s;
+    beam_moe_status st = to_shape(shape, &s);
+    if (st != BEAM_MOE_OK) return st;
+    Post p;
+    p.w = post_w;
+    p.layer = layer;
+    p.resid = resid;
+    p.resid_out = resid_out;
+    if (!y || !aligned(y)) return BEAM_MOE_ERR_INVALID_ARG;
+    if ((st = check_post(s, p)) != BEAM_MOE_OK) return st;
+    if (s.T == 0) return BEAM_MOE_OK;
+    (void)hipGetLastError();
+    beam::launch_post_residual(s, y, post_w, layer, resid, resid_out, (hipStream_t)stream);
+    return hip_status();
 }
 
 const char* beam_moe_status_string(beam_moe_status status) {

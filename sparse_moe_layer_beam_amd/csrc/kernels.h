@@ -48,4 +48,11 @@ void launch_down(const Shape& s, const void* h, const int32_t* offsets, const in
                  hipStream_t st);
 void launch_combine(const Shape& s, const float* y_perm, const int32_t* pair_rank, float* y, hipStream_t st);
 
+// Post-MLP RMSNorm + depth-scaled residual (residual.hip); rows of up to kPostMaxD floats.
+constexpr int kPostMaxD = 16384;
+void launch_combine_post_residual(const Shape& s, const float* y_perm, const int32_t* pair_rank, const void* post_w,
+                                  int layer, const float* resid, float* resid_out, float* y, hipStream_t st);
+void launch_post_residual(const Shape& s, const float* y, const void* post_w, int layer, const float* resid,
+                          float* resid_out, hipStream_t st);
+
 }  // namespace beam

@@ -119,6 +119,37 @@ def test_null_and_misaligned_pointers_are_rejected():
         moe.beam_moe_dispatch(s, A, A, A, None, ws_small, stream=0)
 
 
+def test_residual_entry_points_validate_before_launching():
+    s = beam()
+    n = moe.beam_moe_workspace_bytes(s)
+
+    class WS:
+        def data_ptr(self):
+            return A
+
+        def numel(self):
+            return n - 1
+
+        def element_size(self):
+            return 1
+
+    ws_small = WS()
+    f = lambda *a: moe.beam_moe_forward_residual(s, *a, stream=0, check=False)
+    # args: x, norm_w, Wr, bias, Wg, Wu, Wd, post_w, layer, resid, resid_out, y, idx, w, logits, ws
+    assert f(A, None, A, A, A, A, A, A, 3, A, A, None, None, None, None, ws_small) == WS_SMALL   # y optional
+    assert f(A, None, A, A, A, A, A, None, 3, A, A, A, None, None, None, ws_small) == INVALID    # post_w missing
+    assert f(A, None, A, A, A, A, A, A, -1, A, A, A, None, None, None, ws_small) == INVALID      # layer < 0
+    assert f(A, None, A, A, A, A, A, A, 3, A + 4, A, A, None, None, None, ws_small) == INVALID   # misaligned resid
+    assert f(A, None, A, A, A, A, A, A, 3, A, None, A, None, None, None, ws_small) == INVALID    # resid_out missing
+    p = lambda sh, *a: moe.beam_moe_post_residual(sh, *a, stream=0, check=False)
+    assert p(s, None, A, 3, A, A) == INVALID                                  # y missing
+    assert p(s, A, A, -2, A, A) == INVALID
+    assert p(beam(d=16384 + 64), A, A, 3, A, A) == UNSUPPORTED                # row longer than a block holds
+    assert p(beam(T=0), A, A, 3, A, A) == OK
+    assert moe.beam_moe_forward_residual(beam(T=0), A, None, A, A, A, A, A, A, 0, A, A, None, None, None, None,
+                                         None, stream=0, check=False) == OK
+
+
 def test_zero_tokens_returns_ok_without_workspace():
     s = beam(T=0)
     assert moe.beam_moe_forward(s, A, None, A, A, A, A, A, A, None, None, None, None, stream=0, check=False) == OK
