@@ -1,60 +1,205 @@
 // Tiled grouped GEMM for batches with many tokens per expert (prefill): the gate/up
 // projection with SwiGLU fused in the epilogue, and the down projection with the routing
-// weight fused in the epilogue. BF16 MFMA (v_mfma_f32_32x32x16_bf16), FP32 accumulation.
+// weight fused in the epilogue. BF16 MFMA (v_mfma_f32_16x16x32_bf16), FP32 accumulation.
 //
 // Method: Transformers "Beam" model page (Overview: sparse MoE item, FP32 SwiGLU note;
 // BeamConfig: moe_intermediate_size, hidden_act) and archdb "Beam-1.0-501B-A23B" fact
 // sheet (FFN rows: SwiGLU without biases).
 //
-// Tile: 128 tokens of one expert x 256 weight rows (gate/up: 128 gate + the matching 128 up
-// channels; down: 256 output channels), K staged through LDS 64 at a time, double-buffered.
-// Eight waves (two per SIMD, so one wave's MFMAs cover the other's stalls), each a 64-token
-// x 64-row register tile (4 MFMA tiles of 32x32, 64 FP32 accumulators per lane); a 4-wave
-// variant with 64x128 wave tiles is kept behind BEAM_GEMM_WAVES. The weight rows are the MFMA A operand and the tokens the B
-// operand, so each lane ends up holding 4 consecutive output channels of one token.
+// Tile: up to 128 tokens of one expert x 256 weight rows (gate/up: 128 gate channels and
+// the same 128 up channels; down: 256 output channels). Four waves, one per SIMD, each
+// owning 64 weight rows (four 16-row MFMA subtiles) against all the tile's tokens: a
+// 128 x 64 register tile, 128 FP32 accumulators per lane, so two blocks share a CU and
+// one block's MFMAs run while the other waits on memory.
+//
+// Why this shape on gfx950:
+//  * A weight row is used by one wave only, so weights skip LDS and stream from global
+//    memory straight into registers in MFMA operand layout, one LDS stage ahead. Only the
+//    tokens, which every wave needs, are staged through LDS (64 k at a time,
+//    double-buffered, one barrier per stage). Per flop this needs half the LDS reads of a
+//    both-operands-in-LDS tile with 64x64 wave tiles and a third of its LDS writes.
+//  * The 16x16x32 operand layout gives four lanes to a row, so one weight load covers 16
+//    rows x 64 contiguous bytes (in the 32x32x16 layout a load touches 32 rows x 32 bytes).
+//  * Operands are buffer resources: base and size in scalar registers, one 32-bit offset
+//    per row in a vector register, and loads past the end return zeros.
+// What bounds it (measured on MI355X at T = 8192): removing every MFMA leaves the time
+// unchanged, removing the weight loads halves it. The kernel is bound by the operand
+// traffic from L2 into the CUs (each weight byte is read once per 128-token tile of its
+// expert, tokens once per 256-row weight block), not by the MFMAs or LDS.
 #include "common.h"
 #include "kernels.h"
 
 namespace beam {
 namespace {
 
-constexpr int GBM = 128;             // tokens per tile
-constexpr int GBK = 64;              // k per LDS stage
-constexpr int GBR = 256;             // weight rows per tile
-constexpr int LROW = GBK + 8;        // padded LDS row (bf16): 144 B keeps ds_read_b128 conflict-free
-constexpr int A_ELEMS = GBM * LROW;
-constexpr int B_ELEMS = GBR * LROW;
-constexpr int STAGE = A_ELEMS + B_ELEMS;
-#ifndef BEAM_GEMM_WAVES
-#define BEAM_GEMM_WAVES 8       // 8: two waves per SIMD, 64x64 wave tiles; 4: 64x128 wave tiles
+#ifndef BEAM_GEMM_M
+#define BEAM_GEMM_M 128
 #endif
-constexpr int NW = BEAM_GEMM_WAVES;
-constexpr int NT = 64 * NW;                 // threads per block
-constexpr int LR = NT / 8;                  // rows covered by one 16-byte-per-thread sweep
-constexpr int NQ = NW == 8 ? 2 : 4;         // 32-row weight subtiles per wave
-constexpr int AL = GBM / LR, BL = GBR / LR; // 16-byte loads per thread per stage
-
-__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
+constexpr int GM = BEAM_GEMM_M;      // tokens per tile
+constexpr int kBlocksPerCU = GM == 128 ? 2 : 1;
+constexpr int GN = 256;              // weight rows per tile (4 waves x 64)
+constexpr int GK = 64;               // k per LDS stage (two MFMA k-steps of 32)
+constexpr int LROW = GK + 8;         // padded LDS row (bf16): 144 B keeps ds_read_b128 conflict-free
+constexpr int TILE = GM * LROW;      // one LDS stage
+constexpr int NT = 256;              // threads per block
+constexpr int PAIRS = GM / 32;       // 32-token groups per tile (the unit of partial-tile trimming)
+constexpr int LOADS = GM * GK * 2 / (NT * 16);   // 16-byte token loads per thread per stage
+constexpr int kFrag = 4;             // token fragments read ahead of the MFMAs
+#ifndef BEAM_GEMM_RING
+#define BEAM_GEMM_RING 2
+#endif
+constexpr int RW = BEAM_GEMM_RING;   // stages of weights held in registers (RW-1 in flight)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ void gload(u32x4 (&ra)[AL], u32x4 (&rb)[BL], const u16* const (&a_src)[AL],
-                                      const u16* const (&b_src)[BL], int k) {
-#pragma unroll
-    for (int i = 0; i < AL; ++i) ra[i] = *reinterpret_cast<const u32x4*>(a_src[i] + k);
-#pragma unroll
-    for (int i = 0; i < BL; ++i) rb[i] = *reinterpret_cast<const u32x4*>(b_src[i] + k);
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ void lstore(u16* stage, const u32x4 (&ra)[AL], const u32x4 (&rb)[BL], int lrow,
-                                       int lcol) {
-    u16* B = stage + A_ELEMS;
+// Global operands as buffer resources: the base and size live in scalar registers and each
+// lane keeps one 32-bit byte offset per row, so the loads cost few vector registers (that
+// is what lets the weight prefetch run several stages deep). A load past the resource's
+// size returns zeros instead of faulting.
+constexpr uint32_t kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9 family)
+
+struct Operands {
+    __amdgpu_buffer_rsrc_t w0, w1;   // weight subtiles 0,1 and 2,3 (gate/up: gate and up)
+    __amdgpu_buffer_rsrc_t a;        // token rows
+    uint32_t wv0, wv1;               // this lane's weight row offsets (subtile q even / odd), bytes
+    uint32_t av[LOADS];              // this thread's token row offsets, bytes
+};
+
+__device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+
+// Weight registers of one stage: [k-step j][subtile q]; lane holds row lane%16 of subtile q,
+// k = 64*s + 32*j + 8*(lane/16) .. +8 (kbytes = 128*s). Subtiles 0,1 come from w0 and 2,3
+// from w1, the odd one 16 rows after the even one.
+__device__ __forceinline__ void load_weights(bf16x8 (&w)[2][4], const Operands& op, uint32_t kbytes) {
 #pragma unroll
-    for (int i = 0; i < AL; ++i) *reinterpret_cast<u32x4*>(stage + (lrow + LR * i) * LROW + lcol) = ra[i];
+    for (int q = 0; q < 4; ++q)
 #pragma unroll
-    for (int i = 0; i < BL; ++i) *reinterpret_cast<u32x4*>(B + (lrow + LR * i) * LROW + lcol) = rb[i];
+        for (int j = 0; j < 2; ++j)
+            w[j][q] = __builtin_bit_cast(bf16x8, bload(q < 2 ? op.w0 : op.w1, (q & 1 ? op.wv1 : op.wv0) + 64 * j,
+                                                       kbytes));
+}
+
+// One LDS stage s (k = 64*s .. +64) for a tile whose first 32*LIVE tokens hold the real
+// ones. PAR = s % 2 picks the weight registers; both are template arguments so every
+// register array index is a compile-time constant and the stage has no branches.
+template <int PAR, int LIVE>
+__device__ __forceinline__ void gemm_stage(int s, int nstages, const u16* cur, u16* next,
+                                           f32x4 (&acc)[2 * LIVE][4], bf16x8 (&wr)[RW][2][4], const Operands& op,
+                                           u32x4 (&stg)[LOADS], int st_off, int frag) {
+    constexpr int NS = 2 * LIVE;     // 16-token subtiles
+    // tokens of stage s+1 into registers (the last stage re-reads itself: in bounds, unused)
+    const int kn = min(s + 1, nstages - 1) * GK;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) stg[i] = bload(op.a, op.av[i], 2 * kn);
+    // Token fragments stream through a ring of kFrag registers over the (k-step, subtile)
+    // sequence, so each ds_read is issued kFrag-1 fragments before it is needed.
+    constexpr int NF = 2 * NS;
+    bf16x8 xr[kFrag];
+#pragma unroll
+    for (int f = 0; f < kFrag; ++f)
+        if (f < NF) xr[f] = *reinterpret_cast<const bf16x8*>(cur + 16 * (f % NS) * LROW + frag + 32 * (f / NS));
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+        const int j = f / NS, i = f % NS;
+        const bf16x8 x = xr[f % kFrag];
+        if (f + kFrag < NF) {
+            const int g = f + kFrag;
+            xr[f % kFrag] = *reinterpret_cast<const bf16x8*>(cur + 16 * (g % NS) * LROW + frag + 32 * (g / NS));
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[i][q] = mfma16(wr[PAR][j][q], x, acc[i][q]);
+        // keep the read-ahead where it is: left alone, the scheduler sinks each ds_read to
+        // its MFMAs and the LDS latency is paid in full every time
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // this stage's weight registers take stage s+RW (clamped: in bounds, unused)
+    load_weights(wr[PAR], op, 2 * GK * min(s + RW, nstages - 1));
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) *reinterpret_cast<u32x4*>(next + st_off + 32 * i * LROW) = stg[i];
+    __syncthreads();
+}
+
+// Stages s+P .. s+RW-1 of one ring period; LDS buffers alternate (RW is even).
+template <int P, int LIVE>
+__device__ __forceinline__ void gemm_period(int s, int nstages, u16* lds, f32x4 (&acc)[2 * LIVE][4],
+                                            bf16x8 (&wr)[RW][2][4], const Operands& op, u32x4 (&stg)[LOADS],
+                                            int st_off, int frag) {
+    if constexpr (P < RW) {
+        gemm_stage<P, LIVE>(s + P, nstages, lds + (P & 1) * TILE, lds + ((P + 1) & 1) * TILE, acc, wr, op, stg,
+                            st_off, frag);
+        gemm_period<P + 1, LIVE>(s, nstages, lds, acc, wr, op, stg, st_off, frag);
+    }
+}
+
+// Everything after the work-item decode, for a tile with LIVE live 32-token groups.
+template <int MODE, int LIVE>
+__device__ __forceinline__ void gemm_tile(u16* lds, const Operands& op, int Kdim, int Ndim, int rows,
+                                          size_t orow0, int c0, int lane, const int32_t* __restrict__ pair_of_row,
+                                          const float* __restrict__ topk_w, void* __restrict__ out) {
+    constexpr int NS = 2 * LIVE;
+    f32x4 acc[NS][4];
+#pragma unroll
+    for (int i = 0; i < NS; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[i][q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    const int nstages = Kdim / GK;   // Kdim is a multiple of RW*GK
+    bf16x8 wr[RW][2][4];
+#pragma unroll
+    for (int r = 0; r < RW; ++r) load_weights(wr[r], op, 2 * GK * min(r, nstages - 1));
+    const int tid = threadIdx.x;
+    const int st_off = (tid >> 3) * LROW + (tid & 7) * 8;
+    u32x4 stg[LOADS];
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) stg[i] = bload(op.a, op.av[i], 0);
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) *reinterpret_cast<u32x4*>(lds + st_off + 32 * i * LROW) = stg[i];
+    __syncthreads();
+
+    // token operand (MFMA B: lane holds token lane%16 of a subtile, k 8*(lane/16) .. +8)
+    const int frag = (lane & 15) * LROW + (lane >> 4) * 8;
+    for (int s = 0; s < nstages; s += RW)
+        gemm_period<0, LIVE>(s, nstages, lds, acc, wr, op, stg, st_off, frag);
+
+    // Epilogue. acc[i][q][v]: token 16*i + lane%16 of the tile, row 4*(lane/16) + v of
+    // subtile q, i.e. channel c0 + 16*q' + 4*(lane/16) + v with q' = q (down) or q % 2
+    // (gate/up: q = 0,1 gate and q = 2,3 up of the same channels).
+    const int tcol = lane & 15, rsub = 4 * (lane >> 4);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        const int r = 16 * i + tcol;
+        if (r >= rows) continue;
+        const size_t orow = orow0 + r;
+        if constexpr (MODE == 0) {
+            u16* h = reinterpret_cast<u16*>(out);
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int ch = c0 + 16 * q + rsub;
+                if (ch >= Ndim) continue;
+                const uint32_t lo = (uint32_t)f32_to_bf16(silu_mul(acc[i][q][0], acc[i][q + 2][0])) |
+                                    ((uint32_t)f32_to_bf16(silu_mul(acc[i][q][1], acc[i][q + 2][1])) << 16);
+                const uint32_t hi = (uint32_t)f32_to_bf16(silu_mul(acc[i][q][2], acc[i][q + 2][2])) |
+                                    ((uint32_t)f32_to_bf16(silu_mul(acc[i][q][3], acc[i][q + 2][3])) << 16);
+                *reinterpret_cast<uint2*>(h + orow * Ndim + ch) = make_uint2(lo, hi);
+            }
+        } else {
+            float* y = reinterpret_cast<float*>(out);
+            const float wt = topk_w[pair_of_row[r]];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int ch = c0 + 16 * q + rsub;
+                if (ch >= Ndim) continue;
+                *reinterpret_cast<float4*>(y + orow * Ndim + ch) =
+                    make_float4(wt * acc[i][q][0], wt * acc[i][q][1], wt * acc[i][q][2], wt * acc[i][q][3]);
+            }
+        }
+    }
 }
 
 // MODE 0: out = h [P, I] bf16 = bf16(silu(act . Wg^T) * (act . Wu^T)), act = x rows gathered
@@ -62,12 +207,12 @@ __device__ __forceinline__ void lstore(u16* stage, const u32x4 (&ra)[AL], const 
 // MODE 1: out = y_perm [P, d] fp32 = w_pair * (act . Wd^T), act = h rows in sorted order;
 //         W0 = Wd [E, Ndim, Kdim].
 template <int MODE>
-__global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(
+__global__ __launch_bounds__(NT, kBlocksPerCU) void grouped_gemm_kernel(
         const u16* __restrict__ act, const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pairs,
         const int32_t* __restrict__ tiles, const int32_t* __restrict__ n_tiles_p, const u16* __restrict__ W0,
         const u16* __restrict__ W1, const float* __restrict__ topk_w, int top_k, void* __restrict__ out, int Kdim,
-        int Ndim, int n_nb) {
-    __shared__ __align__(16) u16 lds[2 * STAGE];
+        int Ndim, int n_nb, int act_rows) {
+    __shared__ __align__(16) u16 lds[2 * TILE];
 
     // Work item -> (expert, n-block, m-tile). Blocks are dispatched to the 8 XCDs round-robin
     // (block b on XCD b % 8); XCD x takes the contiguous item range [x*per_xcd, (x+1)*per_xcd),
@@ -86,181 +231,96 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(
     const int mt = local - nb * cnt;
     const int beg = offsets[e];
     const int n_e = offsets[e + 1] - beg;
-    const int m0 = mt * GBM;
-    const int rows = min(GBM, n_e - m0);
-    const int n0 = nb * (MODE == 0 ? GBR / 2 : GBR);
+    const int m0 = mt * GM;
+    const int rows = min(GM, n_e - m0);
+    const int live = min(PAIRS, (rows + 31) / 32);   // 32-token groups holding real tokens
 
-    // Global -> LDS roles: thread t moves 16 B at column (t%8)*8 of rows t/8 + LR*i.
-    const int tid = threadIdx.x;
+    // Token staging: thread t moves 16 B at column (t%8)*8 of tile rows t/8 + 32*i.
+    // Rows past the end of the expert's segment repeat its last row.
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lrow = tid >> 3, lcol = (tid & 7) * 8;
-    const u16* a_src[AL];
+    Operands op;
+    op.a = __builtin_amdgcn_make_buffer_rsrc(const_cast<u16*>(act), (short)0, 2 * act_rows * Kdim, kRsrcWord3);
 #pragma unroll
-    for (int i = 0; i < AL; ++i) {
-        const int m = m0 + min(lrow + LR * i, rows - 1);   // rows past the end repeat a valid row
-        size_t row;
-        if constexpr (MODE == 0) row = (size_t)(sorted_pairs[beg + m] / top_k);
-        else row = (size_t)(beg + m);
-        a_src[i] = act + row * Kdim + lcol;
+    for (int i = 0; i < LOADS; ++i) {   // gemm_supports keeps these offsets below 2^32
+        const int m = m0 + min(lrow + 32 * i, rows - 1);
+        uint32_t row;
+        if constexpr (MODE == 0) row = (uint32_t)(sorted_pairs[beg + m] / top_k);
+        else row = (uint32_t)(beg + m);
+        op.av[i] = 2 * (row * (uint32_t)Kdim + lcol);
     }
-    const u16* b_src[BL];
-#pragma unroll
-    for (int i = 0; i < BL; ++i) {
-        const int r = lrow + LR * i;
-        if constexpr (MODE == 0) {
-            const u16* W = r < GBR / 2 ? W0 : W1;
-            const int ch = min(n0 + (r & (GBR / 2 - 1)), Ndim - 1);
-            b_src[i] = W + ((size_t)e * Ndim + ch) * Kdim + lcol;
-        } else {
-            const int ch = min(n0 + r, Ndim - 1);
-            b_src[i] = W0 + ((size_t)e * Ndim + ch) * Kdim + lcol;
-        }
+    // Weight operand (MFMA A: lane holds row lane%16 of a 16-row subtile, k 8*(lane/16) .. +8
+    // of each 32-wide k-step). The wave's channels start at c0; the expert's base pointers
+    // stay in scalar registers.
+    int c0;
+    const u16* We0 = W0 + (size_t)e * Ndim * Kdim;
+    const uint32_t wbytes = 2u * (uint32_t)Ndim * (uint32_t)Kdim;    // one expert's matrix
+    if constexpr (MODE == 0) {
+        c0 = nb * (GN / 2) + 32 * wave;                 // 32 channels: gate rows, then up rows
+        op.w0 = __builtin_amdgcn_make_buffer_rsrc(const_cast<u16*>(We0), (short)0, wbytes, kRsrcWord3);
+        op.w1 = __builtin_amdgcn_make_buffer_rsrc(const_cast<u16*>(W1 + (size_t)e * Ndim * Kdim), (short)0, wbytes,
+                                                  kRsrcWord3);
+    } else {
+        c0 = nb * GN + 64 * wave;                       // 64 output channels
+        op.w0 = __builtin_amdgcn_make_buffer_rsrc(const_cast<u16*>(We0), (short)0, wbytes, kRsrcWord3);
+        op.w1 = __builtin_amdgcn_make_buffer_rsrc(const_cast<u16*>(We0 + 32 * (size_t)Kdim), (short)0,
+                                                  wbytes - 64u * (uint32_t)Kdim, kRsrcWord3);
     }
-    u32x4 ra0[AL], rb0[BL], ra1[AL], rb1[BL];
-    // Wave tile: tokens [64*wm, +64) as 2 subtiles; NQ weight subtiles of 32 rows. For the
-    // gate/up pass the first half of the subtiles are gate rows and the second half the up
-    // rows of the same channels.
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;   // wave id in an SGPR
-    const int wm = wave & 1, wn = wave >> 1;
-    constexpr int WROWS = NQ * 32;              // weight rows per wave
-    int wrow[NQ];
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-        if constexpr (MODE == 0) wrow[q] = (q < NQ / 2 ? 0 : GBR / 2) + (WROWS / 2) * wn + 32 * (q % (NQ / 2));
-        else wrow[q] = WROWS * wn + 32 * q;
-    }
-    const int frag = (lane & 31) * LROW + (lane >> 5) * 8;
-    f32x16 acc[2][NQ];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int q = 0; q < NQ; ++q)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][q][v] = 0.0f;
+    // rows past Ndim (a partial last n-block) are clamped in bounds; their results are dropped
+    const int last = Ndim - (MODE == 0 ? 32 : 64);
+    op.wv0 = 2 * ((uint32_t)(min(c0, last) + (lane & 15)) * Kdim + (lane >> 4) * 8);
+    op.wv1 = op.wv0 + 32u * (uint32_t)Kdim;             // 16 rows further
 
-    // Token subtiles of this wave that hold at least one real token (the rest of a partial
-    // tile is padding: its MFMAs are skipped).
-    const int live = min(2, max(0, (rows - 64 * wm + 31) / 32));
-
-    // Pipeline (Kdim is a multiple of 2*GBK): LDS holds stage kt (being multiplied) and receives stage kt+1 from registers
-    // loaded one step earlier; the loads for stage kt+2 are in flight meanwhile. The last
-    // prefetches re-read the final stage (in bounds, never consumed), so there is no branch.
-    const int nk = Kdim / GBK;
-    gload(ra0, rb0, a_src, b_src, 0);
-    lstore(lds, ra0, rb0, lrow, lcol);
-    gload(ra1, rb1, a_src, b_src, min(1, nk - 1) * GBK);
-    __syncthreads();
-    // One LDS stage: 4 sub-steps of k=16; the fragments of sub-step kk+1 are read from LDS
-    // while the 8 MFMAs of sub-step kk run.
-    auto mma_stage = [&](const u16* A) {
-        const u16* B = A + A_ELEMS;
-        bf16x8 w[2][NQ], x[2][2];
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) w[0][q] = *reinterpret_cast<const bf16x8*>(B + wrow[q] * LROW + frag);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) x[0][i] = *reinterpret_cast<const bf16x8*>(A + (64 * wm + 32 * i) * LROW + frag);
-#pragma unroll
-        for (int kk = 0; kk < GBK / 16; ++kk) {
-            const int c = kk & 1, n = c ^ 1;
-            if (kk + 1 < GBK / 16) {
-#pragma unroll
-                for (int q = 0; q < NQ; ++q)
-                    w[n][q] = *reinterpret_cast<const bf16x8*>(B + wrow[q] * LROW + frag + 16 * (kk + 1));
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-                    x[n][i] = *reinterpret_cast<const bf16x8*>(A + (64 * wm + 32 * i) * LROW + frag + 16 * (kk + 1));
-            }
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-                if (i < live)
-#pragma unroll
-                    for (int q = 0; q < NQ; ++q) acc[i][q] = mfma32(w[c][q], x[c][i], acc[i][q]);
-        }
-    };
-    for (int kt = 0; kt < nk; kt += 2) {
-        gload(ra0, rb0, a_src, b_src, min(kt + 2, nk - 1) * GBK);
-        mma_stage(lds);
-        lstore(lds + STAGE, ra1, rb1, lrow, lcol);
-        __syncthreads();
-        gload(ra1, rb1, a_src, b_src, min(kt + 3, nk - 1) * GBK);
-        mma_stage(lds + STAGE);
-        lstore(lds, ra0, rb0, lrow, lcol);
-        __syncthreads();
-    }
-
-    // Epilogue. acc[i][q][v]: token 64*wm + 32*i + lane%32 of the tile, weight row
-    // wrow[q] + 8*(v/4) + 4*(lane/32) + v%4.
-    const int tcol = lane & 31, rsub = 4 * (lane >> 5);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int r = 64 * wm + 32 * i + tcol;
-        if (r >= rows) continue;
-        const size_t orow = (size_t)(beg + m0 + r);
-        if constexpr (MODE == 0) {
-            u16* h = reinterpret_cast<u16*>(out);
-#pragma unroll
-            for (int q = 0; q < NQ / 2; ++q)
-#pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) {
-                    const int ch = n0 + (WROWS / 2) * wn + 32 * q + 8 * g4 + rsub;
-                    if (ch >= Ndim) continue;
-                    uint32_t pk[2];
-#pragma unroll
-                    for (int h2 = 0; h2 < 2; ++h2) {
-                        const int v = 4 * g4 + 2 * h2;
-                        pk[h2] = (uint32_t)f32_to_bf16(silu_mul(acc[i][q][v], acc[i][q + NQ / 2][v])) |
-                                 ((uint32_t)f32_to_bf16(silu_mul(acc[i][q][v + 1], acc[i][q + NQ / 2][v + 1]))
-                                  << 16);
-                    }
-                    *reinterpret_cast<uint2*>(h + orow * Ndim + ch) = make_uint2(pk[0], pk[1]);
-                }
-        } else {
-            float* y = reinterpret_cast<float*>(out);
-            const float wt = topk_w[sorted_pairs[beg + m0 + r]];
-#pragma unroll
-            for (int q = 0; q < NQ; ++q)
-#pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) {
-                    const int ch = n0 + WROWS * wn + 32 * q + 8 * g4 + rsub;
-                    if (ch >= Ndim) continue;
-                    const int v = 4 * g4;
-                    *reinterpret_cast<float4*>(y + orow * Ndim + ch) =
-                        make_float4(wt * acc[i][q][v], wt * acc[i][q][v + 1], wt * acc[i][q][v + 2],
-                                    wt * acc[i][q][v + 3]);
-                }
-        }
+    const size_t orow0 = (size_t)(beg + m0);
+    const int32_t* pair_of_row = sorted_pairs + beg + m0;
+    switch (live) {
+#define BEAM_GEMM_CASE(L)                                                                                       \
+    case L:                                                                                                     \
+        gemm_tile<MODE, L>(lds, op, Kdim, Ndim, rows, orow0, c0, lane, pair_of_row, topk_w, out);              \
+        break;
+        BEAM_GEMM_CASE(1) BEAM_GEMM_CASE(2) BEAM_GEMM_CASE(3) BEAM_GEMM_CASE(4)
+#if BEAM_GEMM_M > 128
+        BEAM_GEMM_CASE(5) BEAM_GEMM_CASE(6) BEAM_GEMM_CASE(7) BEAM_GEMM_CASE(8)
+#endif
+#undef BEAM_GEMM_CASE
     }
 }
 
 int max_items(const Shape& s, int n_nb) {
     const int64_t P = s.T * s.K;
-    const int64_t max_tiles = (P + GBM - 1) / GBM + s.E;
+    const int64_t max_tiles = (P + GM - 1) / GM + s.E;
     return (int)(max_tiles * n_nb);
 }
 
 }  // namespace
 
-int gemm_tile_m() { return GBM; }
+int gemm_tile_m() { return GM; }
 
-bool gemm_supports(const Shape& s) { return s.d % (2 * GBK) == 0 && s.I % (2 * GBK) == 0; }
+bool gemm_supports(const Shape& s) {
+    const int64_t P = s.T * s.K;
+    return s.d % (RW * GK) == 0 && s.I % (RW * GK) == 0 && s.T * s.d < (int64_t)INT32_MAX &&
+           P * s.I < (int64_t)INT32_MAX && (int64_t)s.d * s.I < (int64_t)INT32_MAX;   // byte sizes below 2^32
+}
 
 void launch_gemm_swiglu(const Shape& s, const void* x, const int32_t* offsets, const int32_t* sorted_pairs,
                         const int32_t* tiles, const int32_t* n_tiles, const void* Wg, const void* Wu, void* h,
                         hipStream_t st) {
-    const int n_nb = (s.I + GBR / 2 - 1) / (GBR / 2);
+    const int n_nb = (s.I + GN / 2 - 1) / (GN / 2);
     const int blocks = (max_items(s, n_nb) + 7) / 8 * 8;
     hipLaunchKernelGGL(grouped_gemm_kernel<0>, dim3((unsigned)blocks), dim3(NT), 0, st, (const u16*)x, offsets,
                        sorted_pairs, tiles, n_tiles, (const u16*)Wg, (const u16*)Wu, nullptr, s.K, h, s.d, s.I,
-                       n_nb);
+                       n_nb, (int)s.T);
 }
 
 void launch_gemm_down(const Shape& s, const void* h, const int32_t* offsets, const int32_t* sorted_pairs,
                       const float* topk_w, const int32_t* tiles, const int32_t* n_tiles, const void* Wd,
                       float* y_perm, hipStream_t st) {
-    const int n_nb = (s.d + GBR - 1) / GBR;
+    const int n_nb = (s.d + GN - 1) / GN;
     const int blocks = (max_items(s, n_nb) + 7) / 8 * 8;
     hipLaunchKernelGGL(grouped_gemm_kernel<1>, dim3((unsigned)blocks), dim3(NT), 0, st, (const u16*)h, offsets,
                        sorted_pairs, tiles, n_tiles, (const u16*)Wd, nullptr, topk_w, s.K, y_perm, s.I, s.d,
-                       n_nb);
+                       n_nb, (int)(s.T * s.K));
 }
 
 }  // namespace beam
