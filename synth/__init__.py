@@ -12,7 +12,7 @@ import subprocess
 
 import numpy as np
 
-from .recipes import (WORKLOADS, Workload, TID_X, TID_WR, TID_BIAS, TID_WG, TID_WU, TID_WD,
+from .recipes import (WORKLOADS, Workload, DENSE_WORKLOADS, DenseWorkload, TID_X, TID_WR, TID_BIAS, TID_WG, TID_WU, TID_WD,
                       TID_H, TID_NORMW, TID_HOT, TID_RESID, TID_POSTW)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -202,5 +202,40 @@ def device_inputs(w: Workload, device="cuda"):
                                   ("Wd", TID_WD, w.std_down, (w.E, w.d, w.I))):
         ten = torch.empty(shape, dtype=torch.bfloat16, device=device)
         dev_normal(ten.data_ptr(), n, w.seed, tid, 0.0, std, BF16, stream=stream)
+        t[name] = ten
+    return t
+
+
+# ---------------------------------------------------------------------------------------------
+# Dense SwiGLU MLP workloads.
+
+def dense_hidden(w: DenseWorkload, rows=None) -> np.ndarray:
+    """x, [T, d] bf16 bits (optionally only the given rows)."""
+    if rows is None:
+        return host_normal(w.T * w.d, w.seed, TID_X, 0.0, 1.0, BF16).reshape(w.T, w.d)
+    out = np.empty((len(rows), w.d), dtype=np.uint16)
+    for i, r in enumerate(rows):
+        host_normal(w.d, w.seed, TID_X, 0.0, 1.0, BF16, start=int(r) * w.d, out=out[i])
+    return out
+
+
+def dense_weights(w: DenseWorkload):
+    """(Wg [I, d], Wu [I, d], Wd [d, I]) as bf16 bits, generated on the host."""
+    n = w.I * w.d
+    wg = host_normal(n, w.seed, TID_WG, 0.0, w.std_in, BF16).reshape(w.I, w.d)
+    wu = host_normal(n, w.seed, TID_WU, 0.0, w.std_in, BF16).reshape(w.I, w.d)
+    wd = host_normal(n, w.seed, TID_WD, 0.0, w.std_down, BF16).reshape(w.d, w.I)
+    return wg, wu, wd
+
+
+def dense_device_inputs(w: DenseWorkload, device="cuda"):
+    """x, Wg, Wu, Wd of a dense workload generated in HBM (same values as the host twins)."""
+    import torch
+    stream = torch.cuda.current_stream().cuda_stream
+    t = {}
+    for name, tid, std, shape in (("x", TID_X, 1.0, (w.T, w.d)), ("Wg", TID_WG, w.std_in, (w.I, w.d)),
+                                  ("Wu", TID_WU, w.std_in, (w.I, w.d)), ("Wd", TID_WD, w.std_down, (w.d, w.I))):
+        ten = torch.empty(shape, dtype=torch.bfloat16, device=device)
+        dev_normal(ten.data_ptr(), ten.numel(), w.seed, tid, 0.0, std, BF16, stream=stream)
         t[name] = ten
     return t

@@ -81,3 +81,39 @@ WORKLOADS = {
     3: Workload(3, "beam_skewed_T4096", T=4096, hot_experts=16, hot_bias=0.5, **_BEAM),
     4: Workload(4, "beam_chunk_T32768_prenorm", T=32768, prenorm=True, **_BEAM),
 }
+
+
+@dataclass(frozen=True)
+class DenseWorkload:
+    """One dense SwiGLU MLP (the first layers of the model): y = Wd . bf16(silu(Wg . x) * (Wu . x)).
+    Inputs use the MoE tensor ids (x: TID_X, Wg: TID_WG, Wu: TID_WU, Wd: TID_WD) under this
+    workload's own seed; Wg, Wu are [I, d] and Wd is [d, I]."""
+    cfg_id: int
+    name: str
+    T: int
+    d: int
+    I: int
+    seed_base: int = 1000
+
+    @property
+    def seed(self) -> int:
+        return self.seed_base + self.cfg_id
+
+    @property
+    def std_in(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    @property
+    def std_down(self) -> float:
+        return 1.0 / math.sqrt(self.I)
+
+    def with_T(self, T: int) -> "DenseWorkload":
+        from dataclasses import replace
+        return replace(self, T=T)
+
+
+DENSE_WORKLOADS = {
+    10: DenseWorkload(10, "beam_dense_prefill_T8192", T=8192, d=5120, I=20480),
+    11: DenseWorkload(11, "beam_dense_decode_T64", T=64, d=5120, I=20480),
+    12: DenseWorkload(12, "dense_mid_T300", T=300, d=512, I=2048),
+}

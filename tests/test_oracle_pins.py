@@ -319,6 +319,29 @@ def test_rmsnorm_matches_torch_float64():
 
 # --- post-MLP norm and depth-scaled residual ------------------------------------------------
 
+def test_dense_layer_shape_facts():
+    """The dense MLP workloads use the pages' intermediate size, and the dense + MoE layer
+    counts add up to the model's depth."""
+    g = json.load(open(os.path.join(GOLDEN, "beam_shape_facts.json")))
+    for w in recipes.DENSE_WORKLOADS.values():
+        if w.d == 5120:
+            assert w.I == g["intermediate_size"]["value"]
+    assert g["dense_layers"]["value"] + g["moe_layers"]["value"] == g["num_hidden_layers"]["value"]
+    # a dense MLP holds 3*d*I parameters: 8x the intermediate width of one routed expert
+    assert g["intermediate_size"]["value"] == 8 * g["moe_intermediate_size"]["value"]
+
+
+def test_dense_mlp_is_the_single_expert_case():
+    """The dense MLP is the layer's expert arithmetic with one expert and weight 1: moe_rows
+    with K = 1, w = 1 equals expert() on the same rows, bit for bit."""
+    w = recipes.DENSE_WORKLOADS[12].with_T(5)
+    x = synth.dense_hidden(w)
+    wg, wu, wd = synth.dense_weights(w)
+    o = oracle.expert(x, wg, wu, wd)
+    y = oracle.moe_rows(x, np.zeros((w.T, 1), np.int32), np.ones((w.T, 1)), {0: (wg, wu, wd)}, 1)
+    assert np.array_equal(o, y)
+
+
 def test_residual_step_telescopes_to_sum_over_sqrt_k():
     """After contributions c_1..c_m the stream is their sum over sqrt(m), the property the
     Beam page states for the depth-scaled residual. A wrong k offset, a swapped keep/add
