@@ -160,6 +160,21 @@ beam_moe_status beam_moe_forward_residual(const beam_moe_shape* shape, const voi
                                           float* logits, void* workspace, size_t ws_bytes, void* stream,
                                           void* const* stage_events);
 
+/* Dense SwiGLU MLP of the first decoder layers (Transformers "Beam" page, Overview: the
+ * first 3 layers use a dense SwiGLU MLP; BeamConfig: intermediate_size, hidden_act):
+ *   y = Wd . bf16(silu(Wg . x) * (Wu . x))   per token, BF16 MFMA with FP32 accumulation,
+ * h rounded to bf16 once as in the experts; no routing, no scaling.
+ *   T, d, I    tokens, hidden size (5120), intermediate size (20480); d and I multiples of
+ *              128 with T*d, T*I and d*I below 2^31 (else BEAM_MOE_ERR_UNSUPPORTED_SHAPE)
+ *   x          [T, d] bf16
+ *   Wg, Wu     [I, d] bf16;  Wd [d, I] bf16
+ *   y          [T, d] FP32 out
+ *   workspace  at least beam_moe_dense_workspace_bytes(T, d, I) bytes (holds h [T, I] bf16)
+ * T = 0 returns BEAM_MOE_OK with no launch. */
+size_t beam_moe_dense_workspace_bytes(int64_t T, int32_t d, int32_t I);
+beam_moe_status beam_moe_dense_mlp(int64_t T, int32_t d, int32_t I, const void* x, const void* Wg, const void* Wu,
+                                   const void* Wd, float* y, void* workspace, size_t ws_bytes, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* beam_moe_status_string(beam_moe_status status);
 

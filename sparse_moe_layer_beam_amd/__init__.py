@@ -21,7 +21,7 @@ BEAM_MOE_ERR_HIP = 4
 
 EXPORTED = ("beam_moe_workspace_bytes", "beam_moe_route", "beam_moe_dispatch", "beam_moe_forward",
             "beam_moe_forward_staged", "beam_moe_post_residual", "beam_moe_forward_residual",
-            "beam_moe_status_string")
+            "beam_moe_dense_workspace_bytes", "beam_moe_dense_mlp", "beam_moe_status_string")
 N_STAGE_EVENTS = 6
 
 
@@ -74,6 +74,10 @@ def lib() -> ctypes.CDLL:
         L.beam_moe_forward_residual.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp,
                                                 vp, sz, vp, vp]
         L.beam_moe_forward_residual.restype = i32
+        L.beam_moe_dense_workspace_bytes.argtypes = [ctypes.c_int64, i32, i32]
+        L.beam_moe_dense_workspace_bytes.restype = sz
+        L.beam_moe_dense_mlp.argtypes = [ctypes.c_int64, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.beam_moe_dense_mlp.restype = i32
         L.beam_moe_status_string.argtypes = [i32]
         L.beam_moe_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -175,3 +179,13 @@ def beam_moe_forward_residual(shape, x, norm_w, Wr, bias, Wg, Wu, Wd, post_w, la
                                          _ptr(y), _ptr(topk_idx), _ptr(topk_w), _ptr(logits), _ptr(workspace),
                                          _nbytes(workspace), _stream(stream), _events(stage_events))
     return _check(st, "beam_moe_forward_residual") if check else st
+
+
+def beam_moe_dense_workspace_bytes(T: int, d: int, I: int) -> int:
+    return int(lib().beam_moe_dense_workspace_bytes(int(T), int(d), int(I)))
+
+
+def beam_moe_dense_mlp(T, d, I, x, Wg, Wu, Wd, y, workspace, stream=None, check=True) -> int:
+    st = lib().beam_moe_dense_mlp(int(T), int(d), int(I), _ptr(x), _ptr(Wg), _ptr(Wu), _ptr(Wd), _ptr(y),
+                                  _ptr(workspace), _nbytes(workspace), _stream(stream))
+    return _check(st, "beam_moe_dense_mlp") if check else st

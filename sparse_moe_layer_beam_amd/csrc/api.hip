@@ -257,6 +257,27 @@ beam_moe_status beam_moe_post_residual(const beam_moe_shape* shape, const float*
     return hip_status();
 }
 
+size_t beam_moe_dense_workspace_bytes(int64_t T, int32_t d, int32_t I) {
+    if (T < 0 || d <= 0 || I <= 0) return 0;
+    return up((size_t)T * (size_t)I * 2);
+}
+
+beam_moe_status beam_moe_dense_mlp(int64_t T, int32_t d, int32_t I, const void* x, const void* Wg, const void* Wu,
+                                   const void* Wd, float* y, void* workspace, size_t ws_bytes, void* stream) {
+    if (T < 0 || d <= 0 || I <= 0) return BEAM_MOE_ERR_INVALID_ARG;
+    if (!x || !Wg || !Wu || !Wd || !y) return BEAM_MOE_ERR_INVALID_ARG;
+    if (!aligned(x) || !aligned(Wg) || !aligned(Wu) || !aligned(Wd) || !aligned(y)) return BEAM_MOE_ERR_INVALID_ARG;
+    if (!beam::dense_supports(T, d, I)) return BEAM_MOE_ERR_UNSUPPORTED_SHAPE;
+    if (T == 0) return BEAM_MOE_OK;
+    if (!workspace || !aligned(workspace)) return BEAM_MOE_ERR_INVALID_ARG;
+    if (ws_bytes < beam_moe_dense_workspace_bytes(T, d, I)) return BEAM_MOE_ERR_WORKSPACE_TOO_SMALL;
+    hipStream_t hs = (hipStream_t)stream;
+    (void)hipGetLastError();
+    beam::launch_dense_swiglu(T, d, I, x, Wg, Wu, workspace, hs);
+    beam::launch_dense_down(T, d, I, workspace, Wd, y, hs);
+    return hip_status();
+}
+
 const char* beam_moe_status_string(beam_moe_status status) {
     switch (status) {
         case BEAM_MOE_OK: return "ok";

@@ -190,7 +190,7 @@ __device__ __forceinline__ void gemm_tile(u16* lds, const Operands& op, int Kdim
             }
         } else {
             float* y = reinterpret_cast<float*>(out);
-            const float wt = topk_w[pair_of_row[r]];
+            const float wt = topk_w ? topk_w[pair_of_row[r]] : 1.0f;   // NULL: dense MLP, weight 1
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int ch = c0 + 16 * q + rsub;
@@ -206,7 +206,9 @@ __device__ __forceinline__ void gemm_tile(u16* lds, const Operands& op, int Kdim
 //         through sorted_pairs (token = pair / top_k); W0 = Wg, W1 = Wu, both [E, Ndim, Kdim].
 // MODE 1: out = y_perm [P, d] fp32 = w_pair * (act . Wd^T), act = h rows in sorted order;
 //         W0 = Wd [E, Ndim, Kdim].
-template <int MODE>
+// DENSE: one expert holding all act_rows tokens in order (the dense SwiGLU MLP): no tile
+//         list, no gather, weight 1; MODE 1 then writes y [T, d] directly.
+template <int MODE, bool DENSE>
 __global__ __launch_bounds__(NT, kBlocksPerCU) void grouped_gemm_kernel(
         const u16* __restrict__ act, const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pairs,
         const int32_t* __restrict__ tiles, const int32_t* __restrict__ n_tiles_p, const u16* __restrict__ W0,
@@ -218,19 +220,30 @@ __global__ __launch_bounds__(NT, kBlocksPerCU) void grouped_gemm_kernel(
     // (block b on XCD b % 8); XCD x takes the contiguous item range [x*per_xcd, (x+1)*per_xcd),
     // ordered expert, n-block, m-tile, so the m-tiles sharing one weight tile run together
     // on one XCD and the tile comes from HBM about once.
-    const int n_items = *n_tiles_p * n_nb;
+    const int n_mt_dense = (act_rows + GM - 1) / GM;
+    const int n_items = DENSE ? n_mt_dense * n_nb : *n_tiles_p * n_nb;
     const int per_xcd = (n_items + 7) / 8;
     const int slot = blockIdx.x >> 3;
     if (slot >= per_xcd) return;
     const int item = (blockIdx.x & 7) * per_xcd + slot;
     if (item >= n_items) return;
-    const int j = item / n_nb;                 // a tile of the item's expert
-    const int e = tiles[4 * j], first = tiles[4 * j + 2], cnt = tiles[4 * j + 3];
-    const int local = item - first * n_nb;
-    const int nb = local / cnt;
-    const int mt = local - nb * cnt;
-    const int beg = offsets[e];
-    const int n_e = offsets[e + 1] - beg;
+    int e, nb, mt, beg, n_e;
+    if constexpr (DENSE) {
+        e = 0;
+        nb = item / n_mt_dense;
+        mt = item - nb * n_mt_dense;
+        beg = 0;
+        n_e = act_rows;
+    } else {
+        const int j = item / n_nb;                 // a tile of the item's expert
+        e = tiles[4 * j];
+        const int first = tiles[4 * j + 2], cnt = tiles[4 * j + 3];
+        const int local = item - first * n_nb;
+        nb = local / cnt;
+        mt = local - nb * cnt;
+        beg = offsets[e];
+        n_e = offsets[e + 1] - beg;
+    }
     const int m0 = mt * GM;
     const int rows = min(GM, n_e - m0);
     const int live = min(PAIRS, (rows + 31) / 32);   // 32-token groups holding real tokens
@@ -246,7 +259,7 @@ __global__ __launch_bounds__(NT, kBlocksPerCU) void grouped_gemm_kernel(
     for (int i = 0; i < LOADS; ++i) {   // gemm_supports keeps these offsets below 2^32
         const int m = m0 + min(lrow + 32 * i, rows - 1);
         uint32_t row;
-        if constexpr (MODE == 0) row = (uint32_t)(sorted_pairs[beg + m] / top_k);
+        if constexpr (MODE == 0 && !DENSE) row = (uint32_t)(sorted_pairs[beg + m] / top_k);
         else row = (uint32_t)(beg + m);
         op.av[i] = 2 * (row * (uint32_t)Kdim + lcol);
     }
@@ -273,7 +286,7 @@ __global__ __launch_bounds__(NT, kBlocksPerCU) void grouped_gemm_kernel(
     op.wv1 = op.wv0 + 32u * (uint32_t)Kdim;             // 16 rows further
 
     const size_t orow0 = (size_t)(beg + m0);
-    const int32_t* pair_of_row = sorted_pairs + beg + m0;
+    const int32_t* pair_of_row = DENSE ? nullptr : sorted_pairs + beg + m0;
     switch (live) {
 #define BEAM_GEMM_CASE(L)                                                                                       \
     case L:                                                                                                     \
@@ -308,7 +321,7 @@ void launch_gemm_swiglu(const Shape& s, const void* x, const int32_t* offsets, c
                         hipStream_t st) {
     const int n_nb = (s.I + GN / 2 - 1) / (GN / 2);
     const int blocks = (max_items(s, n_nb) + 7) / 8 * 8;
-    hipLaunchKernelGGL(grouped_gemm_kernel<0>, dim3((unsigned)blocks), dim3(NT), 0, st, (const u16*)x, offsets,
+    hipLaunchKernelGGL((grouped_gemm_kernel<0, false>), dim3((unsigned)blocks), dim3(NT), 0, st, (const u16*)x, offsets,
                        sorted_pairs, tiles, n_tiles, (const u16*)Wg, (const u16*)Wu, nullptr, s.K, h, s.d, s.I,
                        n_nb, (int)s.T);
 }
@@ -318,9 +331,34 @@ void launch_gemm_down(const Shape& s, const void* h, const int32_t* offsets, con
                       float* y_perm, hipStream_t st) {
     const int n_nb = (s.d + GN - 1) / GN;
     const int blocks = (max_items(s, n_nb) + 7) / 8 * 8;
-    hipLaunchKernelGGL(grouped_gemm_kernel<1>, dim3((unsigned)blocks), dim3(NT), 0, st, (const u16*)h, offsets,
+    hipLaunchKernelGGL((grouped_gemm_kernel<1, false>), dim3((unsigned)blocks), dim3(NT), 0, st, (const u16*)h, offsets,
                        sorted_pairs, tiles, n_tiles, (const u16*)Wd, nullptr, topk_w, s.K, y_perm, s.I, s.d,
                        n_nb, (int)(s.T * s.K));
+}
+
+// Dense SwiGLU MLP (one expert, all T tokens in order): h = bf16(silu(x . Wg^T) * (x . Wu^T)),
+// then y = h . Wd^T in FP32.
+void launch_dense_swiglu(int64_t T, int d, int I, const void* x, const void* Wg, const void* Wu, void* h,
+                         hipStream_t st) {
+    const int n_nb = (I + GN / 2 - 1) / (GN / 2);
+    const int items = (int)((T + GM - 1) / GM) * n_nb;
+    hipLaunchKernelGGL((grouped_gemm_kernel<0, true>), dim3((unsigned)((items + 7) / 8 * 8)), dim3(NT), 0, st,
+                       (const u16*)x, nullptr, nullptr, nullptr, nullptr, (const u16*)Wg, (const u16*)Wu, nullptr, 1,
+                       h, d, I, n_nb, (int)T);
+}
+
+void launch_dense_down(int64_t T, int d, int I, const void* h, const void* Wd, float* y, hipStream_t st) {
+    const int n_nb = (d + GN - 1) / GN;
+    const int items = (int)((T + GM - 1) / GM) * n_nb;
+    hipLaunchKernelGGL((grouped_gemm_kernel<1, true>), dim3((unsigned)((items + 7) / 8 * 8)), dim3(NT), 0, st,
+                       (const u16*)h, nullptr, nullptr, nullptr, nullptr, (const u16*)Wd, nullptr, nullptr, 1, y, I, d,
+                       n_nb, (int)T);
+}
+
+bool dense_supports(int64_t T, int d, int I) {
+    Shape s{};
+    s.T = T; s.d = d; s.I = I; s.K = 1; s.E = 1;
+    return gemm_supports(s);
 }
 
 }  // namespace beam

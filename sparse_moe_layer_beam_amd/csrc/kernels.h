@@ -48,6 +48,12 @@ void launch_down(const Shape& s, const void* h, const int32_t* offsets, const in
                  hipStream_t st);
 void launch_combine(const Shape& s, const float* y_perm, const int32_t* pair_rank, float* y, hipStream_t st);
 
+// Dense SwiGLU MLP through the same GEMM (grouped_gemm.hip).
+bool dense_supports(int64_t T, int d, int I);
+void launch_dense_swiglu(int64_t T, int d, int I, const void* x, const void* Wg, const void* Wu, void* h,
+                         hipStream_t st);
+void launch_dense_down(int64_t T, int d, int I, const void* h, const void* Wd, float* y, hipStream_t st);
+
 // Post-MLP RMSNorm + depth-scaled residual (residual.hip); rows of up to kPostMaxD floats.
 constexpr int kPostMaxD = 16384;
 void launch_combine_post_residual(const Shape& s, const float* y_perm, const int32_t* pair_rank, const void* post_w,

@@ -150,6 +150,33 @@ def test_residual_entry_points_validate_before_launching():
                                          None, stream=0, check=False) == OK
 
 
+def test_dense_mlp_validates_before_launching():
+    n = moe.beam_moe_dense_workspace_bytes(64, 5120, 20480)
+    assert n >= 64 * 20480 * 2
+    assert moe.beam_moe_dense_workspace_bytes(-1, 5120, 20480) == 0
+
+    class WS:
+        def __init__(self, nbytes):
+            self.n = nbytes
+
+        def data_ptr(self):
+            return A
+
+        def numel(self):
+            return self.n
+
+        def element_size(self):
+            return 1
+
+    f = lambda T, d, I, *a: moe.beam_moe_dense_mlp(T, d, I, *a, stream=0, check=False)
+    assert f(64, 5120, 20480, A, A, A, A, A, WS(n - 1)) == WS_SMALL
+    assert f(64, 5120, 20480, None, A, A, A, A, WS(n)) == INVALID          # x missing
+    assert f(64, 5120, 20480, A, A, A, A, A + 4, WS(n)) == INVALID         # misaligned y
+    assert f(64, 5120 + 64, 20480, A, A, A, A, A, WS(n)) == UNSUPPORTED    # d not a multiple of 128
+    assert f(-3, 5120, 20480, A, A, A, A, A, WS(n)) == INVALID
+    assert f(0, 5120, 20480, A, A, A, A, A, None) == OK
+
+
 def test_zero_tokens_returns_ok_without_workspace():
     s = beam(T=0)
     assert moe.beam_moe_forward(s, A, None, A, A, A, A, A, A, None, None, None, None, stream=0, check=False) == OK

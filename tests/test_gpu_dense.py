@@ -1,0 +1,63 @@
+"""Dense SwiGLU MLP on the GPU (beam_moe_dense_mlp, through the C ABI) against the oracle's
+expert() in double: every token at mid size and at ragged token counts, sampled tokens at
+the Beam dense shape (d=5120, I=20480), bitwise run-to-run determinism."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle
+import synth
+import sparse_moe_layer_beam_amd as moe
+from synth import recipes
+from tests import _parity as P
+
+pytestmark = pytest.mark.gpu
+
+MID = recipes.DENSE_WORKLOADS[12]
+
+
+def _run(w, t):
+    ws = torch.empty(max(1, moe.beam_moe_dense_workspace_bytes(w.T, w.d, w.I)), dtype=torch.uint8, device="cuda")
+    y = torch.full((w.T, w.d), float("nan"), dtype=torch.float32, device="cuda")
+    moe.beam_moe_dense_mlp(w.T, w.d, w.I, t["x"], t["Wg"], t["Wu"], t["Wd"], y, ws)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+@pytest.fixture(autouse=True)
+def _free_gpu():
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("T", [1, 77, 129, 300])
+def test_dense_mid_every_token(T):
+    w = MID.with_T(T)
+    print("case dense mid T", T, flush=True)
+    t = synth.dense_device_inputs(w)
+    y = _run(w, t)
+    ref = oracle.expert(synth.dense_hidden(w), *synth.dense_weights(w))
+    err, rms = P.output_error(y, ref)
+    print("dense mid T=%d: max|dy| %.3e, rms %.3e" % (T, err, rms))
+    assert np.isfinite(y).all()
+    assert err <= P.Y_TOL * rms
+
+
+@pytest.mark.parametrize("cfg", [10, 11])
+def test_dense_beam_shape_sampled(cfg):
+    w = recipes.DENSE_WORKLOADS[cfg]
+    print("case dense beam", w.name, flush=True)
+    t = synth.dense_device_inputs(w)
+    y = _run(w, t)
+    y2 = _run(w, t)
+    assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+    rng = np.random.default_rng(cfg)
+    rows = sorted({0, w.T - 1, *rng.choice(w.T, size=min(6, w.T), replace=False).tolist()})
+    wg, wu, wd = synth.dense_weights(w)
+    ref = oracle.expert(synth.dense_hidden(w, rows), wg, wu, wd)
+    err, rms = P.output_error(y[rows], ref)
+    print("%s: %d sampled tokens, max|dy| %.3e, rms %.3e" % (w.name, len(rows), err, rms))
+    assert np.isfinite(y).all()
+    assert err <= P.Y_TOL * rms
