@@ -48,6 +48,13 @@ def lib():
         L.oracle_residual_step.argtypes = [vp, vp, i64, i32, vp]
         L.oracle_contribution_index.argtypes = [i32, i32]
         L.oracle_contribution_index.restype = i32
+        L.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
+        L.oracle_e4m3_value.restype = dbl
+        L.oracle_e4m3_round.argtypes = [dbl]
+        L.oracle_e4m3_round.restype = ctypes.c_uint8
+        L.oracle_fp8_quantize.argtypes = [vp, i64, i32, vp, vp, i32]
+        L.oracle_fp8_dequantize.argtypes = [vp, vp, i64, i32, vp]
+        L.oracle_fp8_dequantize.restype = i64
         _lib = L
     return _lib
 
@@ -199,3 +206,35 @@ def post_residual(y, w, eps, resid, layer):
     """MoE output y [T,d] -> residual stream after the MLP of 0-indexed layer `layer` (float64)."""
     k = contribution_index(layer, True)
     return residual_step(resid, post_norm(y, w, eps), k)
+
+
+def e4m3_value(code: int) -> float:
+    return float(lib().oracle_e4m3_value(int(code)))
+
+
+def e4m3_round(v: float) -> int:
+    return int(lib().oracle_e4m3_round(float(v)))
+
+
+def fp8_quantize(w: np.ndarray):
+    """[rows, K] bf16 bits -> (q [rows, K] uint8 E4M3 codes, s [rows, K/32] uint8 E8M0 scales)."""
+    w = _c(w, np.uint16)
+    rows, K = w.shape
+    if K % 32:
+        raise ValueError("K must be a multiple of 32")
+    q = np.empty((rows, K), dtype=np.uint8)
+    s = np.empty((rows, K // 32), dtype=np.uint8)
+    lib().oracle_fp8_quantize(w.ctypes.data, rows, K, q.ctypes.data, s.ctypes.data, nthreads())
+    return q, s
+
+
+def fp8_dequantize(q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """-> [rows, K] bf16 bits of 2^(s-127) * e4m3(q); raises if any value is not exact in bf16."""
+    q = _c(q, np.uint8)
+    s = _c(s, np.uint8)
+    rows, K = q.shape
+    out = np.empty((rows, K), dtype=np.uint16)
+    bad = lib().oracle_fp8_dequantize(q.ctypes.data, s.ctypes.data, rows, K, out.ctypes.data)
+    if bad:
+        raise ValueError("%d dequantized values are not exact in bf16" % bad)
+    return out

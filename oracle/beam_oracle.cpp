@@ -40,6 +40,12 @@
 //   - the SwiGLU output h is rounded to bf16 once before the down projection
 //     (the down projection is a bf16 GEMM); y is reported without rounding;
 //   - the RMSNorm output is rounded to bf16 once, x = bf16((h * r) * w).
+//   - FP8 expert weights (decode, optional): the pages name FP8 checkpoints but no scaling
+//     recipe, so the oracle takes the OCP Microscaling (MX) v1.0 FP8 layout: E4M3 elements
+//     (OCP 8-bit floating point, bias 7, largest finite 448, no infinities) sharing one
+//     power-of-two E8M0 scale per 32 consecutive k of a row, shared exponent
+//     floor(log2(max |w|)) - 8, elements rounded to nearest even and saturated to +-448;
+//     a block of zeros takes scale 2^0. The layer then runs on the dequantized weights.
 //   - the post-MLP RMSNorm reads the unrounded y and is not rounded either: the
 //     residual stream it feeds is accumulated in FP32 (archdb fact sheet, residual row).
 //
@@ -306,5 +312,75 @@ void oracle_residual_step(const double* r, const double* c, int64_t n, int32_t k
 // first, then attention and MLP of each layer in turn (0-indexed layer i: attention 2(i+1),
 // MLP 2(i+1)+1).
 int32_t oracle_contribution_index(int32_t layer, int32_t is_mlp) { return 2 * (layer + 1) + (is_mlp ? 1 : 0); }
+
+
+// ---- FP8 (OCP E4M3) weights with one power-of-two scale per 32 values (OCP MX) ----------
+
+// Value of an E4M3 code: sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent field 0
+// holds the subnormals m/8 * 2^-6; exponent 15 with mantissa 7 is NaN.
+double oracle_e4m3_value(uint8_t c) {
+    const int sgn = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    double v;
+    if (e == 15 && m == 7) return std::nan("");
+    if (e == 0) v = std::ldexp((double)m, -9);
+    else v = std::ldexp(1.0 + m / 8.0, e - 7);
+    return sgn ? -v : v;
+}
+
+// Nearest E4M3 code to v, ties to the even mantissa, magnitudes at or above 448 saturated.
+uint8_t oracle_e4m3_round(double v) {
+    const uint8_t sgn = std::signbit(v) ? 0x80 : 0x00;
+    const double a = std::fabs(v);
+    if (a >= 448.0) return sgn | 0x7E;
+    int ex;
+    std::frexp(a, &ex);          // a = f * 2^ex, f in [0.5, 1): floor(log2 a) = ex - 1
+    int e = ex - 1;
+    if (a == 0.0 || e < -6) {    // subnormal range: multiples of 2^-9
+        const int m = (int)std::nearbyint(std::ldexp(a, 9));
+        return sgn | (uint8_t)m; // m == 8 is the code of 2^-6, the smallest normal
+    }
+    int m = (int)std::nearbyint((std::ldexp(a, -e) - 1.0) * 8.0);
+    if (m == 8) {
+        m = 0;
+        ++e;
+    }
+    return sgn | (uint8_t)(((e + 7) << 3) | m);
+}
+
+// Quantize a [rows, K] bf16 matrix (K % 32 == 0) into E4M3 codes q [rows, K] and E8M0 scale
+// bytes s [rows, K/32]: block b of row r holds 2^(s - 127) * e4m3(q).
+void oracle_fp8_quantize(const uint16_t* w, int64_t rows, int32_t K, uint8_t* q, uint8_t* s, int32_t nthreads) {
+    const int nb = K / 32;
+    parallel_for(rows, nthreads, [&](int64_t r) {
+        for (int b = 0; b < nb; ++b) {
+            const uint16_t* blk = w + r * K + 32 * b;
+            double amax = 0.0;
+            for (int i = 0; i < 32; ++i) amax = std::max(amax, std::fabs(bf16_value(blk[i])));
+            int shared = 0;
+            if (amax > 0.0) {
+                int ex;
+                std::frexp(amax, &ex);
+                shared = std::min(127, std::max(-127, (ex - 1) - 8));
+            }
+            s[r * nb + b] = (uint8_t)(shared + 127);
+            for (int i = 0; i < 32; ++i) q[r * K + 32 * b + i] = oracle_e4m3_round(std::ldexp(bf16_value(blk[i]), -shared));
+        }
+    });
+}
+
+// Dequantize back to bf16 bits (the products are exact in bf16 for every scale >= 2^-118,
+// i.e. any trained weight); returns the number of elements that were not exact.
+int64_t oracle_fp8_dequantize(const uint8_t* q, const uint8_t* s, int64_t rows, int32_t K, uint16_t* out) {
+    const int nb = K / 32;
+    int64_t inexact = 0;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int k = 0; k < K; ++k) {
+            const double v = std::ldexp(oracle_e4m3_value(q[r * K + k]), (int)s[r * nb + k / 32] - 127);
+            const uint16_t b = bf16_round(v);
+            if (bf16_value(b) != v) ++inexact;
+            out[r * K + k] = b;
+        }
+    return inexact;
+}
 
 }  // extern "C"

@@ -403,3 +403,93 @@ def test_post_norm_closed_forms_and_torch():
     yt = torch.from_numpy(y)
     ref = yt * torch.rsqrt(yt.pow(2).mean(-1, keepdim=True) + eps) * torch.from_numpy(wv)
     np.testing.assert_allclose(oracle.post_norm(y, nw, eps), ref.numpy(), rtol=1e-14, atol=0)
+
+
+# --- FP8 (OCP E4M3 elements, MX block scales) ------------------------------------------------
+
+def test_e4m3_decode_matches_torch_and_ocp_anchors():
+    """Every one of the 256 codes decodes like torch's float8_e4m3fn (NaN where it has NaN),
+    and the defining values of the OCP E4M3 format sit where the standard puts them."""
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).double().numpy()
+    got = np.array([oracle.e4m3_value(c) for c in range(256)])
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(got[fin], ref[fin])
+    anchors = {0x7E: 448.0, 0x08: 2.0 ** -6, 0x07: 0.875 * 2.0 ** -6, 0x01: 2.0 ** -9, 0x38: 1.0, 0xFE: -448.0}
+    for c, v in anchors.items():
+        assert oracle.e4m3_value(c) == v
+    assert np.isnan(oracle.e4m3_value(0x7F)) and np.isnan(oracle.e4m3_value(0xFF))
+
+
+def test_e4m3_round_matches_torch_on_every_bf16_in_range():
+    """Round-to-nearest-even against torch's float8_e4m3fn conversion for every finite bf16
+    value below the first value torch turns into NaN (464); above 448 the oracle saturates."""
+    bits = np.arange(65536, dtype=np.uint32)
+    vals = (bits << 16).view(np.float32)
+    keep = np.isfinite(vals) & (np.abs(vals) < 464.0)
+    vals = vals[keep]
+    ref = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle.e4m3_round(float(v)) for v in vals], dtype=np.uint8)
+    diff = got != ref
+    assert not diff.any(), vals[diff][:8]
+    for v in (448.0, 463.9, 1e4, 1e30):
+        assert oracle.e4m3_round(v) == 0x7E and oracle.e4m3_round(-v) == 0xFE
+
+
+def _grid_matrix(rng, rows, K):
+    """Values exactly on the E4M3 x 2^s grid with one e-field-15 element per block."""
+    nb = K // 32
+    finite = np.array([c for c in range(0x7F) if not np.isnan(oracle.e4m3_value(c))], dtype=np.uint8)
+    q = rng.choice(finite, size=(rows, K)).astype(np.uint8)
+    q |= (rng.integers(0, 2, size=(rows, K)) << 7).astype(np.uint8)
+    top = rng.integers(0x78, 0x7F, size=(rows, nb)).astype(np.uint8)      # exponent field 15
+    pos = rng.integers(0, 32, size=(rows, nb))
+    for r in range(rows):
+        for b in range(nb):
+            q[r, 32 * b + pos[r, b]] = top[r, b] | (q[r, 32 * b + pos[r, b]] & 0x80)
+    s = rng.integers(127 - 20, 127 - 8, size=(rows, nb)).astype(np.uint8)
+    return q, s
+
+
+def test_fp8_quantize_round_trips_grid_values():
+    """A matrix already on the grid (with the block maximum in the top binade) comes back
+    with the same codes and scales: pins the shared-exponent rule and the element rounding."""
+    rng = np.random.default_rng(11)
+    q, s = _grid_matrix(rng, 6, 128)
+    w = oracle.fp8_dequantize(q, s)
+    q2, s2 = oracle.fp8_quantize(w)
+    assert np.array_equal(s2, s)
+    # +0 and -0 are the same value; compare values
+    assert np.array_equal(oracle.fp8_dequantize(q2, s2), w)
+
+
+def test_fp8_quantize_nearest_and_bounds():
+    """On random bf16 weights: each code is the nearest grid value (brute force over all
+    finite codes, ties to the even code), the block maximum lands in [256, 448] * 2^s, and
+    a block of zeros gets scale 2^0."""
+    rng = np.random.default_rng(5)
+    vals = (rng.standard_normal((4, 96)) * 0.02).astype(np.float32)
+    vals[1, 32:64] = 0.0
+    w = _ref.f64_to_bf16_bits_rne(vals.astype(np.float64))
+    q, s = oracle.fp8_quantize(w)
+    wv = _ref.bf16_bits_to_f64(w)
+    grid = np.array([oracle.e4m3_value(c) for c in range(256)])
+    fin = np.nonzero(~np.isnan(grid))[0]
+    for r in range(4):
+        for k in range(96):
+            sc = 2.0 ** (int(s[r, k // 32]) - 127)
+            x = wv[r, k] / sc
+            d = np.abs(grid[fin] - x)
+            best = fin[d == d.min()]
+            best_vals = set(grid[best].tolist())
+            assert grid[q[r, k]] in best_vals or (x == 0 and grid[q[r, k]] == 0)
+            if len(best_vals) > 1:                     # an exact tie: the even mantissa wins
+                assert q[r, k] % 2 == 0
+    assert s[1, 1] == 127 and not (q[1, 32:64] & 0x7F).any()
+    for r in range(4):
+        for b in range(3):
+            if r == 1 and b == 1:
+                continue
+            top = max(abs(grid[c]) for c in q[r, 32 * b: 32 * b + 32])
+            assert 256 <= top <= 448
