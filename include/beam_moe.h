@@ -160,6 +160,31 @@ beam_moe_status beam_moe_forward_residual(const beam_moe_shape* shape, const voi
                                           float* logits, void* workspace, size_t ws_bytes, void* stream,
                                           void* const* stage_events);
 
+/* FP8 expert weights (decode-sized batches). The pages name FP8 checkpoints (news.hamidun.com
+ * article and strelka.ai overview, FP8 weights) but no scaling recipe; the layout here is the
+ * OCP Microscaling (MX) v1.0 FP8 one: E4M3 codes (OCP 8-bit floating point: bias 7, largest
+ * finite 448) and one E8M0 scale byte per 32 consecutive values of a row, value =
+ * 2^(scale - 127) * e4m3(code).
+ *
+ * beam_moe_quantize_fp8: w [rows, K] bf16 -> q [rows, K] codes and scales [rows, K/32] bytes.
+ *   Shared exponent of a block = floor(log2(max |w|)) - 8, clamped to [-127, 127] (0 for a
+ *   block of zeros); each w / 2^shared rounded to the nearest E4M3 value, ties to even,
+ *   saturated to +-448. K % 32 == 0 (else BEAM_MOE_ERR_INVALID_ARG); w and q 16-byte aligned.
+ *   For expert weights call it on Wg and Wu viewed as [E*I, d] and on Wd as [E*d, I]. */
+beam_moe_status beam_moe_quantize_fp8(int64_t rows, int32_t K, const void* w, void* q, void* scales, void* stream);
+
+/* beam_moe_forward_staged with FP8 expert weights: identical routing, dispatch and combine;
+ * the gate/up and down GEMMs read the codes and scales from beam_moe_quantize_fp8 (Wg8, Wu8
+ * [E, I, d], Wd8 [E, d, I], sg, su [E, I, d/32], sd [E, d, I/32]) and widen them exactly to bf16
+ * in registers, so the result is the bf16 layer's on the dequantized weights. Decode-sized
+ * batches only (T * top_k <= 16 * E) with d and I multiples of 512, else
+ * BEAM_MOE_ERR_UNSUPPORTED_SHAPE. All pointers 16-byte aligned. */
+beam_moe_status beam_moe_forward_fp8(const beam_moe_shape* shape, const void* x, const void* norm_w, const float* Wr,
+                                     const float* bias, const void* Wg8, const void* Wu8, const void* Wd8,
+                                     const void* sg, const void* su, const void* sd, float* y, int32_t* topk_idx,
+                                     float* topk_w, float* logits, void* workspace, size_t ws_bytes, void* stream,
+                                     void* const* stage_events);
+
 /* Dense SwiGLU MLP of the first decoder layers (Transformers "Beam" page, Overview: the
  * first 3 layers use a dense SwiGLU MLP; BeamConfig: intermediate_size, hidden_act):
  *   y = Wd . bf16(silu(Wg . x) * (Wu . x))   per token, BF16 MFMA with FP32 accumulation,

@@ -21,7 +21,8 @@ BEAM_MOE_ERR_HIP = 4
 
 EXPORTED = ("beam_moe_workspace_bytes", "beam_moe_route", "beam_moe_dispatch", "beam_moe_forward",
             "beam_moe_forward_staged", "beam_moe_post_residual", "beam_moe_forward_residual",
-            "beam_moe_dense_workspace_bytes", "beam_moe_dense_mlp", "beam_moe_status_string")
+            "beam_moe_dense_workspace_bytes", "beam_moe_dense_mlp", "beam_moe_quantize_fp8",
+            "beam_moe_forward_fp8", "beam_moe_status_string")
 N_STAGE_EVENTS = 6
 
 
@@ -78,6 +79,10 @@ def lib() -> ctypes.CDLL:
         L.beam_moe_dense_workspace_bytes.restype = sz
         L.beam_moe_dense_mlp.argtypes = [ctypes.c_int64, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
         L.beam_moe_dense_mlp.restype = i32
+        L.beam_moe_quantize_fp8.argtypes = [ctypes.c_int64, i32, vp, vp, vp, vp]
+        L.beam_moe_quantize_fp8.restype = i32
+        L.beam_moe_forward_fp8.argtypes = [shp] + [vp] * 14 + [sz, vp, vp]
+        L.beam_moe_forward_fp8.restype = i32
         L.beam_moe_status_string.argtypes = [i32]
         L.beam_moe_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -189,3 +194,17 @@ def beam_moe_dense_mlp(T, d, I, x, Wg, Wu, Wd, y, workspace, stream=None, check=
     st = lib().beam_moe_dense_mlp(int(T), int(d), int(I), _ptr(x), _ptr(Wg), _ptr(Wu), _ptr(Wd), _ptr(y),
                                   _ptr(workspace), _nbytes(workspace), _stream(stream))
     return _check(st, "beam_moe_dense_mlp") if check else st
+
+
+def beam_moe_quantize_fp8(rows, K, w, q, scales, stream=None, check=True) -> int:
+    st = lib().beam_moe_quantize_fp8(int(rows), int(K), _ptr(w), _ptr(q), _ptr(scales), _stream(stream))
+    return _check(st, "beam_moe_quantize_fp8") if check else st
+
+
+def beam_moe_forward_fp8(shape, x, norm_w, Wr, bias, Wg8, Wu8, Wd8, sg, su, sd, y, topk_idx, topk_w, logits,
+                         workspace, stage_events=None, stream=None, check=True) -> int:
+    st = lib().beam_moe_forward_fp8(ctypes.byref(shape), _ptr(x), _ptr(norm_w), _ptr(Wr), _ptr(bias), _ptr(Wg8),
+                                    _ptr(Wu8), _ptr(Wd8), _ptr(sg), _ptr(su), _ptr(sd), _ptr(y), _ptr(topk_idx),
+                                    _ptr(topk_w), _ptr(logits), _ptr(workspace), _nbytes(workspace),
+                                    _stream(stream), _events(stage_events))
+    return _check(st, "beam_moe_forward_fp8") if check else st

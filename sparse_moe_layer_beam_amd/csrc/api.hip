@@ -146,6 +146,19 @@ struct Post {
     float* resid_out = nullptr;
 };
 
+// Optional FP8 expert weights (decode-sized batches): codes and per-32 scale bytes.
+struct Fp8 {
+    const void *Wg, *Wu, *Wd, *sg, *su, *sd;
+};
+
+beam_moe_status check_fp8(const Shape& s, const Fp8& f) {
+    if (!f.Wg || !f.Wu || !f.Wd || !f.sg || !f.su || !f.sd) return BEAM_MOE_ERR_INVALID_ARG;
+    if (!aligned(f.Wg) || !aligned(f.Wu) || !aligned(f.Wd) || !aligned(f.sg) || !aligned(f.su) || !aligned(f.sd))
+        return BEAM_MOE_ERR_INVALID_ARG;
+    if (!beam::fp8_supports(s)) return BEAM_MOE_ERR_UNSUPPORTED_SHAPE;
+    return BEAM_MOE_OK;
+}
+
 beam_moe_status check_post(const Shape& s, const Post& p) {
     if (!p.w || !p.resid || !p.resid_out || p.layer < 0) return BEAM_MOE_ERR_INVALID_ARG;
     if (!aligned(p.w) || !aligned(p.resid) || !aligned(p.resid_out)) return BEAM_MOE_ERR_INVALID_ARG;
@@ -156,10 +169,16 @@ beam_moe_status check_post(const Shape& s, const Post& p) {
 beam_moe_status forward_impl(const beam_moe_shape* shape, const void* x, const void* norm_w, const float* Wr,
                              const float* bias, const void* Wg, const void* Wu, const void* Wd, float* y,
                              int32_t* topk_idx, float* topk_w, float* logits, void* workspace, size_t ws_bytes,
-                             void* stream, void* const* events, const Post* post) {
+                             void* stream, void* const* events, const Post* post, const Fp8* fp8 = nullptr) {
     Shape s;
     beam_moe_status st = to_shape(shape, &s);
     if (st != BEAM_MOE_OK) return st;
+    if (fp8) {
+        if ((st = check_fp8(s, *fp8)) != BEAM_MOE_OK) return st;
+        Wg = fp8->Wg;
+        Wu = fp8->Wu;
+        Wd = fp8->Wd;
+    }
     if (!x || !Wr || !bias || !Wg || !Wu || !Wd || (!y && !post)) return BEAM_MOE_ERR_INVALID_ARG;
     if (!aligned(x) || !aligned(Wr) || !aligned(bias) || !aligned(Wg) || !aligned(Wu) || !aligned(Wd) ||
         (y && !aligned(y)) || (norm_w && !aligned(norm_w)) || (topk_idx && !aligned(topk_idx)) ||
@@ -192,9 +211,15 @@ beam_moe_status forward_impl(const beam_moe_shape* shape, const void* x, const v
     mark(2);
     void* h = at<void>(workspace, L.h);
     float* yp = at<float>(workspace, L.yp);
-    beam::launch_swiglu(s, xin, off, sp, tiles, ntiles, Wg, Wu, h, hs);
+    if (fp8)
+        beam::launch_swiglu_fp8(s, xin, off, sp, fp8->Wg, fp8->Wu, fp8->sg, fp8->su, h, hs);
+    else
+        beam::launch_swiglu(s, xin, off, sp, tiles, ntiles, Wg, Wu, h, hs);
     mark(3);
-    beam::launch_down(s, h, off, sp, w, tiles, ntiles, Wd, yp, hs);
+    if (fp8)
+        beam::launch_down_fp8(s, h, off, sp, w, fp8->Wd, fp8->sd, yp, hs);
+    else
+        beam::launch_down(s, h, off, sp, w, tiles, ntiles, Wd, yp, hs);
     mark(4);
     if (post)
         beam::launch_combine_post_residual(s, yp, pr, post->w, post->layer, post->resid, post->resid_out, y, hs);
@@ -255,6 +280,26 @@ beam_moe_status beam_moe_post_residual(const beam_moe_shape* shape, const float*
     (void)hipGetLastError();
     beam::launch_post_residual(s, y, post_w, layer, resid, resid_out, (hipStream_t)stream);
     return hip_status();
+}
+
+beam_moe_status beam_moe_quantize_fp8(int64_t rows, int32_t K, const void* w, void* q, void* scales, void* stream) {
+    if (rows < 0 || K <= 0 || K % 32 != 0) return BEAM_MOE_ERR_INVALID_ARG;
+    if (!w || !q || !scales || !aligned(w) || !aligned(q)) return BEAM_MOE_ERR_INVALID_ARG;
+    if (rows * (int64_t)K >= ((int64_t)1 << 40)) return BEAM_MOE_ERR_UNSUPPORTED_SHAPE;
+    if (rows == 0) return BEAM_MOE_OK;
+    (void)hipGetLastError();
+    beam::launch_fp8_quantize(rows, K, w, q, scales, (hipStream_t)stream);
+    return hip_status();
+}
+
+beam_moe_status beam_moe_forward_fp8(const beam_moe_shape* shape, const void* x, const void* norm_w, const float* Wr,
+                                     const float* bias, const void* Wg8, const void* Wu8, const void* Wd8,
+                                     const void* sg, const void* su, const void* sd, float* y, int32_t* topk_idx,
+                                     float* topk_w, float* logits, void* workspace, size_t ws_bytes, void* stream,
+                                     void* const* stage_events) {
+    Fp8 f{Wg8, Wu8, Wd8, sg, su, sd};
+    return forward_impl(shape, x, norm_w, Wr, bias, nullptr, nullptr, nullptr, y, topk_idx, topk_w, logits, workspace,
+                        ws_bytes, stream, stage_events, nullptr, &f);
 }
 
 size_t beam_moe_dense_workspace_bytes(int64_t T, int32_t d, int32_t I) {

@@ -48,6 +48,14 @@ void launch_down(const Shape& s, const void* h, const int32_t* offsets, const in
                  hipStream_t st);
 void launch_combine(const Shape& s, const float* y_perm, const int32_t* pair_rank, float* y, hipStream_t st);
 
+// FP8 (OCP E4M3 + one E8M0 scale per 32 values) expert weights for decode (experts_fp8.hip).
+void launch_fp8_quantize(int64_t rows, int K, const void* w, void* q, void* s, hipStream_t st);
+bool fp8_supports(const Shape& s);
+void launch_swiglu_fp8(const Shape& s, const void* x, const int32_t* offsets, const int32_t* sorted_pairs,
+                       const void* Wg8, const void* Wu8, const void* sg, const void* su, void* h, hipStream_t st);
+void launch_down_fp8(const Shape& s, const void* h, const int32_t* offsets, const int32_t* sorted_pairs,
+                     const float* topk_w, const void* Wd8, const void* sd, float* y_perm, hipStream_t st);
+
 // Dense SwiGLU MLP through the same GEMM (grouped_gemm.hip).
 bool dense_supports(int64_t T, int d, int I);
 void launch_dense_swiglu(int64_t T, int d, int I, const void* x, const void* Wg, const void* Wu, void* h,

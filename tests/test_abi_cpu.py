@@ -177,6 +177,38 @@ def test_dense_mlp_validates_before_launching():
     assert f(0, 5120, 20480, A, A, A, A, A, None) == OK
 
 
+def test_fp8_entry_points_validate_before_launching():
+    q = lambda *a: moe.beam_moe_quantize_fp8(*a, stream=0, check=False)
+    assert q(10, 48, A, A, A) == INVALID           # K not a multiple of 32
+    assert q(10, 64, None, A, A) == INVALID
+    assert q(10, 64, A + 2, A, A) == INVALID
+    assert q(0, 64, A, A, A) == OK
+    s = beam()
+    n = moe.beam_moe_workspace_bytes(s)
+
+    class WS:
+        def __init__(self, nbytes):
+            self.n = nbytes
+
+        def data_ptr(self):
+            return A
+
+        def numel(self):
+            return self.n
+
+        def element_size(self):
+            return 1
+
+    f = lambda sh, *a: moe.beam_moe_forward_fp8(sh, *a, stream=0, check=False)
+    # args: x, norm_w, Wr, bias, Wg8, Wu8, Wd8, sg, su, sd, y, idx, w, logits, ws
+    assert f(s, A, None, A, A, A, A, A, A, A, A, A, None, None, None, WS(n - 1)) == WS_SMALL
+    assert f(s, A, None, A, A, A, A, A, A, None, A, A, None, None, None, WS(n)) == INVALID      # su missing
+    big = beam(T=8192)                                                                          # prefill-sized
+    assert f(big, A, None, A, A, A, A, A, A, A, A, A, None, None, None, WS(n)) == UNSUPPORTED
+    odd = beam(d=5120 + 128)                                                                    # d % 512 != 0
+    assert f(odd, A, None, A, A, A, A, A, A, A, A, A, None, None, None, WS(n)) == UNSUPPORTED
+
+
 def test_zero_tokens_returns_ok_without_workspace():
     s = beam(T=0)
     assert moe.beam_moe_forward(s, A, None, A, A, A, A, A, A, None, None, None, None, stream=0, check=False) == OK
