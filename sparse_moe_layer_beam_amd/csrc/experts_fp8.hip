@@ -20,7 +20,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;
-constexpr int kD = 8;   // 64-k steps in flight per wave (one group of scale bytes)
+#ifndef BEAM_FP8_D
+#define BEAM_FP8_D 8
+#endif
+constexpr int kD = BEAM_FP8_D;   // 64-k steps in flight per wave (8: one group of scale bytes)
 
 // ---- quantization --------------------------------------------------------------------------
 
@@ -95,26 +98,34 @@ __device__ __forceinline__ bf16x8 widen(uint32_t lo, uint32_t hi, float sc) {
     return __builtin_bit_cast(bf16x8, w);
 }
 
-// acc[m] += W . X_m^T over k in [0, K), K a multiple of 512, for 16 fp8 weight rows and MT
-// tiles of 16 tokens. In 64-k step t, lane (r = lane%16, c = lane/16) holds bytes
-// 64t + 16c .. +16 of weight row r and elements 64t + 16c .. +16 of its token rows, which
-// feed two MFMAs (elements 0..7, then 8..15): the k order inside a step is the same for both
-// operands, and each weight load covers 16 rows x 64 contiguous bytes.
-// wq: row r + 16c bytes; ws: the row's scale bytes; x: token rows + 16c elements.
-template <int MT>
-__device__ __forceinline__ void stream_fp8(const uint8_t* wq, const uint8_t* ws, const u16* const (&x)[MT], int K,
-                                           int c, f32x4 (&acc)[MT]) {
-    u32x4 wa[kD];
+// acc[m][b] += W_b . X_m^T over k in [0, K), K a multiple of 512, for RB blocks of 16 fp8
+// weight rows and MT tiles of 16 tokens. In 64-k step t, lane (r = lane%16, c = lane/16)
+// holds bytes 64t + 16c .. +16 of row r of each block and elements 64t + 16c .. +16 of its
+// token rows, which feed two MFMAs (elements 0..7, then 8..15): the k order inside a step is
+// the same for both operands, and each weight load covers 16 rows x 64 contiguous bytes.
+// The token fragments of a step serve all RB blocks (for gate/up: the gate and up rows of
+// the same channels), half the activation loads of one pass per block. Measured on MI355X
+// at the decode workload it runs as fast as two passes (a second open row stream per wave
+// costs what the saved loads gain); with 1-byte weights the activation loads, not the
+// weights, hold these kernels below the bf16 kernels' share of HBM bandwidth.
+// wq[b]: row r of block b + 16c bytes; ws[b]: its scale bytes; x: token rows + 16c elements.
+template <int RB, int MT>
+__device__ __forceinline__ void stream_fp8(const uint8_t* const (&wq)[RB], const uint8_t* const (&ws)[RB],
+                                           const u16* const (&x)[MT], int K, int c, f32x4 (&acc)[MT][RB]) {
+    u32x4 wa[kD][RB];
     bf16x8 xa[kD][MT][2];
     const int nsteps = K / 64;
     const int last = nsteps - 1;
     // scale bytes of eight steps (16 blocks of 32) per 16-byte load; this lane needs block
     // 2t + c/2 of step t
     const int half = c >> 1;
-    u32x4 sc = *reinterpret_cast<const u32x4*>(ws);
+    u32x4 sc[RB];
+#pragma unroll
+    for (int b = 0; b < RB; ++b) sc[b] = *reinterpret_cast<const u32x4*>(ws[b]);
 #pragma unroll
     for (int t = 0; t < kD; ++t) {
-        wa[t] = *reinterpret_cast<const u32x4*>(wq + 64 * t);
+#pragma unroll
+        for (int b = 0; b < RB; ++b) wa[t][b] = *reinterpret_cast<const u32x4*>(wq[b] + 64 * t);
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
             xa[t][m][0] = *reinterpret_cast<const bf16x8*>(x[m] + 64 * t);
@@ -122,32 +133,41 @@ __device__ __forceinline__ void stream_fp8(const uint8_t* wq, const uint8_t* ws,
         }
     }
     for (int g = 0; g < nsteps; g += kD) {
-        const u32x4 sc_next = *reinterpret_cast<const u32x4*>(ws + 2 * min(g + kD, last - (kD - 1)));
+        u32x4 sc_next[RB];
+#pragma unroll
+        for (int b = 0; b < RB; ++b)
+            sc_next[b] = *reinterpret_cast<const u32x4*>(ws[b] + 2 * min(g + kD, last - (kD - 1)));
 #pragma unroll
         for (int t = 0; t < kD; ++t) {
-            const uint32_t byte = (sc[t >> 1] >> (16 * (t & 1) + 8 * half)) & 0xFFu;
-            const float s = __uint_as_float(byte << 23);           // 2^(byte - 127)
-            const bf16x8 a0 = widen(wa[t][0], wa[t][1], s);
-            const bf16x8 a1 = widen(wa[t][2], wa[t][3], s);
 #pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                acc[m] = mfma16(a0, xa[t][m][0], acc[m]);
-                acc[m] = mfma16(a1, xa[t][m][1], acc[m]);
+            for (int b = 0; b < RB; ++b) {
+                const uint32_t byte = (sc[b][t >> 1] >> (16 * (t & 1) + 8 * half)) & 0xFFu;
+                const float s = __uint_as_float(byte << 23);       // 2^(byte - 127)
+                const bf16x8 a0 = widen(wa[t][b][0], wa[t][b][1], s);
+                const bf16x8 a1 = widen(wa[t][b][2], wa[t][b][3], s);
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    acc[m][b] = mfma16(a0, xa[t][m][0], acc[m][b]);
+                    acc[m][b] = mfma16(a1, xa[t][m][1], acc[m][b]);
+                }
             }
             const int kn = 64 * min(g + kD + t, last);             // clamped: in bounds, unused at the end
-            wa[t] = *reinterpret_cast<const u32x4*>(wq + kn);
+#pragma unroll
+            for (int b = 0; b < RB; ++b) wa[t][b] = *reinterpret_cast<const u32x4*>(wq[b] + kn);
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
                 xa[t][m][0] = *reinterpret_cast<const bf16x8*>(x[m] + kn);
                 xa[t][m][1] = *reinterpret_cast<const bf16x8*>(x[m] + kn + 8);
             }
         }
-        sc = sc_next;
+#pragma unroll
+        for (int b = 0; b < RB; ++b) sc[b] = sc_next[b];
     }
 }
 
 // h[beg+m, n] = bf16(silu(x_m . Wg[e,n]) * (x_m . Wu[e,n])) for the tokens m of expert e, fp8
-// weights. grid: (ceil(I / 64), E); block: 4 waves of 16 output channels (gate rows, then up).
+// weights. grid: (ceil(I / 64), E); block: 4 waves of 16 output channels, each streaming its
+// gate and up rows together.
 __global__ __launch_bounds__(256) void swiglu_fp8_kernel(const u16* __restrict__ x, const int32_t* __restrict__ offsets,
                                                          const int32_t* __restrict__ sorted_pairs, int top_k,
                                                          const uint8_t* __restrict__ Wg, const uint8_t* __restrict__ Wu,
@@ -165,15 +185,17 @@ __global__ __launch_bounds__(256) void swiglu_fp8_kernel(const u16* __restrict__
     for (int mb = 0; mb < n_e; mb += 16) {
         const int m = min(mb + r, n_e - 1);                         // rows past the end repeat a valid row
         const u16* const xp[1] = {x + (size_t)(sorted_pairs[beg + m] / top_k) * d + 16 * c};
-        f32x4 g[1] = {{0, 0, 0, 0}}, u[1] = {{0, 0, 0, 0}};
-        stream_fp8<1>(Wg + row * d + 16 * c, sg + row * (d / 32), xp, d, c, g);
-        stream_fp8<1>(Wu + row * d + 16 * c, su + row * (d / 32), xp, d, c, u);
+        const uint8_t* const wq[2] = {Wg + row * d + 16 * c, Wu + row * d + 16 * c};
+        const uint8_t* const ws[2] = {sg + row * (d / 32), su + row * (d / 32)};
+        f32x4 acc[1][2] = {{{0, 0, 0, 0}, {0, 0, 0, 0}}};
+        stream_fp8<2, 1>(wq, ws, xp, d, c, acc);
+        const f32x4 g = acc[0][0], u = acc[0][1];
         // lane holds channels n0 + 4c + i of token mb + r
         if (mb + r < n_e) {
-            const uint32_t lo = (uint32_t)f32_to_bf16(silu_mul(g[0][0], u[0][0])) |
-                                ((uint32_t)f32_to_bf16(silu_mul(g[0][1], u[0][1])) << 16);
-            const uint32_t hi = (uint32_t)f32_to_bf16(silu_mul(g[0][2], u[0][2])) |
-                                ((uint32_t)f32_to_bf16(silu_mul(g[0][3], u[0][3])) << 16);
+            const uint32_t lo = (uint32_t)f32_to_bf16(silu_mul(g[0], u[0])) |
+                                ((uint32_t)f32_to_bf16(silu_mul(g[1], u[1])) << 16);
+            const uint32_t hi = (uint32_t)f32_to_bf16(silu_mul(g[2], u[2])) |
+                                ((uint32_t)f32_to_bf16(silu_mul(g[3], u[3])) << 16);
             *reinterpret_cast<uint2*>(h + (size_t)(beg + mb + r) * I + n0 + 4 * c) = make_uint2(lo, hi);
         }
     }
@@ -196,12 +218,14 @@ __global__ __launch_bounds__(256) void down_fp8_kernel(const u16* __restrict__ h
     const size_t row = (size_t)e * d + n0 + r;
     for (int mb = 0; mb < n_e; mb += 16) {
         const u16* const hp[1] = {h + (size_t)(beg + min(mb + r, n_e - 1)) * I + 16 * c};
-        f32x4 acc[1] = {{0, 0, 0, 0}};
-        stream_fp8<1>(Wd + row * I + 16 * c, sd + row * (I / 32), hp, I, c, acc);
+        const uint8_t* const wq[1] = {Wd + row * I + 16 * c};
+        const uint8_t* const ws[1] = {sd + row * (I / 32)};
+        f32x4 acc[1][1] = {{{0, 0, 0, 0}}};
+        stream_fp8<1, 1>(wq, ws, hp, I, c, acc);
         if (mb + r < n_e) {
             const float wt = topk_w[sorted_pairs[beg + mb + r]];
             *reinterpret_cast<float4*>(y_perm + (size_t)(beg + mb + r) * d + n0 + 4 * c) =
-                make_float4(wt * acc[0][0], wt * acc[0][1], wt * acc[0][2], wt * acc[0][3]);
+                make_float4(wt * acc[0][0][0], wt * acc[0][0][1], wt * acc[0][0][2], wt * acc[0][0][3]);
         }
     }
 }
