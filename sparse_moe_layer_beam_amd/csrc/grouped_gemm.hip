@@ -18,9 +18,10 @@
 //    weights-straight-to-registers design needs) stop at ~10 TB/s, which bounded the
 //    earlier versions of this kernel.
 //  * A 256 x 256 tile reads 2/256 bytes of operands per flop.
-//  * A stage is 64 KB (256 token rows + 256 weight rows of 128 bytes), double-buffered in
-//    128 KB of LDS: the loads of stage s+1 are issued at the start of stage s and awaited
-//    at its closing barrier.
+//  * A stage is 256 token rows + 256 weight rows of 128 bytes. Token rows come mostly from
+//    L2 and are double-buffered; weight rows come from HBM and are triple-buffered, their
+//    loads issued two stages ahead (160 KB of LDS). The waits before each stage's barrier
+//    are placed by hand: the barrier of __syncthreads would drain every load in flight.
 //  * The direct loads write 1 KB per wave in lane order; each lane picks its source chunk
 //    so that LDS row r holds global 16-byte chunk c at position c ^ (r % 8). The MFMA
 //    fragment reads (16 rows x one chunk) then hit eight different positions per eight
@@ -35,8 +36,10 @@ constexpr int GM = 256;                  // tokens per tile
 constexpr int GN = 256;                  // weight rows per tile
 constexpr int GK = 64;                   // k per stage
 constexpr int NW = 8, NT = 64 * NW;      // waves, threads per block
-constexpr int SROWS = GM + GN;           // LDS rows per stage: tokens, then weights
-constexpr int SELEMS = SROWS * GK;       // bf16 per stage (64 KB)
+constexpr int SROWS = GM + GN;           // rows per stage: tokens (loaded by waves 0-3), then weights (4-7)
+constexpr int TELEMS = GM * GK;          // bf16 of one token buffer (32 KB)
+constexpr int WELEMS = GN * GK;          // bf16 of one weight buffer (32 KB)
+constexpr int NTB = 2, NWB = 3;          // token and weight buffers: 160 KB of LDS
 constexpr int DMA = SROWS / (8 * NW);    // direct loads per wave per stage (8 rows each)
 constexpr int kFrag = 4;                 // token fragments read ahead of the MFMAs
 
@@ -46,20 +49,31 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Direct loads of stage s into one LDS buffer: load i of this wave fills rows
-// 64*wave + 8i .. +8 (1 KB, 1 KB aligned), lane l writing 16 bytes at l*16.
-__device__ __forceinline__ void stage_load(const u16* const (&src)[DMA], int s, u16* buf, int wave) {
+// Direct loads of this wave's 64 rows of stage s into buffer buf (token waves: a token
+// buffer; weight waves: a weight buffer): load i fills rows 8i .. +8 of the wave's part
+// (1 KB, 1 KB aligned), lane l writing 16 bytes at l*16.
+__device__ __forceinline__ void stage_load(const u16* const (&src)[DMA], int s, u16* buf) {
 #pragma unroll
     for (int i = 0; i < DMA; ++i)
-        __builtin_amdgcn_global_load_lds((const void*)(src[i] + s * GK), (lds_void*)(buf + (64 * wave + 8 * i) * GK),
-                                         16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(src[i] + s * GK), (lds_void*)(buf + 8 * i * GK), 16, 0, 0);
+}
+
+// End of a stage: this wave's loads that the next stage needs have landed and its LDS reads
+// are done, then every wave meets. Token waves keep nothing in flight; weight waves keep
+// the loads of the stage after next (DMA instructions) in flight. Written as one asm block
+// so that the compiler neither drains every load at the barrier nor moves memory
+// operations across it.
+__device__ __forceinline__ void stage_end(bool deep) {
+    if (deep) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // One stage: MFMAs of the wave's LIVE 16-token subtiles against its four 16-row weight
-// subtiles, k = 64 from LDS buffer buf. Fragment of global k-chunk c (8 bf16) of LDS row r
-// sits at r*64 + 8*(c ^ (r % 8)); this lane's rows all have r % 8 == lane % 8.
+// subtiles, k = 64, from token buffer tb and weight buffer wb. Fragment of global k-chunk
+// c (8 bf16) of a buffer row r sits at r*64 + 8*(c ^ (r % 8)); this lane's rows all have
+// r % 8 == lane % 8.
 template <int LIVE>
-__device__ __forceinline__ void stage_mma(const u16* buf, int tok0, const int (&wrow)[4], int lane,
+__device__ __forceinline__ void stage_mma(const u16* tb, const u16* wb, int tok0, const int (&wrow)[4], int lane,
                                           f32x4 (&acc)[8][4]) {
     const int lr = lane & 15, sw = lane & 7, c0 = lane >> 4;
 #pragma unroll
@@ -67,17 +81,17 @@ __device__ __forceinline__ void stage_mma(const u16* buf, int tok0, const int (&
         const int pos = ((4 * j + c0) ^ sw) * 8;
         bf16x8 w[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) w[q] = *reinterpret_cast<const bf16x8*>(buf + (wrow[q] + lr) * GK + pos);
+        for (int q = 0; q < 4; ++q) w[q] = *reinterpret_cast<const bf16x8*>(wb + (wrow[q] + lr) * GK + pos);
         if constexpr (LIVE > 0) {
             bf16x8 xr[kFrag];
 #pragma unroll
             for (int f = 0; f < kFrag; ++f)
-                if (f < LIVE) xr[f] = *reinterpret_cast<const bf16x8*>(buf + (tok0 + 16 * f + lr) * GK + pos);
+                if (f < LIVE) xr[f] = *reinterpret_cast<const bf16x8*>(tb + (tok0 + 16 * f + lr) * GK + pos);
 #pragma unroll
             for (int i = 0; i < LIVE; ++i) {
                 const bf16x8 x = xr[i % kFrag];
                 if (i + kFrag < LIVE)
-                    xr[i % kFrag] = *reinterpret_cast<const bf16x8*>(buf + (tok0 + 16 * (i + kFrag) + lr) * GK + pos);
+                    xr[i % kFrag] = *reinterpret_cast<const bf16x8*>(tb + (tok0 + 16 * (i + kFrag) + lr) * GK + pos);
 #pragma unroll
                 for (int q = 0; q < 4; ++q) acc[i][q] = mfma16(w[q], x, acc[i][q]);
                 // keep the read-ahead in place (the scheduler would sink it to its MFMAs)
@@ -99,15 +113,32 @@ __device__ __forceinline__ void gemm_run(u16* lds, const u16* const (&src)[DMA],
 #pragma unroll
         for (int q = 0; q < 4; ++q) acc[i][q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    stage_load(src, 0, lds, wave);
-    __syncthreads();
+    // Token waves load stage s+1 during stage s (two token buffers); weight waves load stage
+    // s+2 (three weight buffers), since weights come from HBM at its loaded latency. Every
+    // wave issues the same number of loads per stage (clamped to the last stage at the end),
+    // which is what the fixed wait counts in stage_end rely on.
+    u16* const tbuf = lds;
+    u16* const wbuf = lds + NTB * TELEMS;
+    const bool weight_wave = wave >= NW / 2;
+    const int part = (weight_wave ? wave - NW / 2 : wave) * 64 * GK;   // this wave's 64 rows of a buffer
+    const int last = nstages - 1;
+    // a wave's ring depth: the buffers of the operand it loads
+    const int nb = weight_wave ? NWB : NTB;
+    u16* const mine = (weight_wave ? wbuf : tbuf) + part;
+    const int belems = weight_wave ? WELEMS : TELEMS;
+    const bool deep = nb == 3;
+    stage_load(src, 0, mine);
+    if (deep) stage_load(src, min(1, last), mine + belems);
+    stage_end(deep);
     for (int s = 0; s < nstages; ++s) {
-        u16* cur = lds + (s & 1) * SELEMS;
-        // the other buffer was last read in stage s-1, which every wave has left
-        if (s + 1 < nstages) stage_load(src, s + 1, lds + ((s + 1) & 1) * SELEMS, wave);
-        stage_mma<LIVE>(cur, tok0, wrow, lane, acc);
-        __syncthreads();   // waits for this wave's loads of stage s+1, then for every wave
+        // the buffer loaded here was last read in stage s-1, which every wave has left
+        const int ahead = nb - 1;
+        stage_load(src, min(s + ahead, last), mine + ((s + ahead) % nb) * belems);
+        stage_mma<LIVE>(tbuf + (s % NTB) * TELEMS, wbuf + (s % NWB) * WELEMS, tok0, wrow, lane, acc);
+        stage_end(deep);
     }
+    // the weight waves' last (clamped, unused) loads must land before the block's LDS is released
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // Epilogue. acc[i][q][v]: token tok0 + 16*i + lane%16 of the tile, channel
     // c0 + 16*q' + 4*(lane/16) + v with q' = q (down) or q % 2 (gate/up: q = 0,1 gate and
@@ -156,7 +187,7 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(
         const int32_t* __restrict__ tiles, const int32_t* __restrict__ n_tiles_p, const u16* __restrict__ W0,
         const u16* __restrict__ W1, const float* __restrict__ topk_w, int top_k, void* __restrict__ out, int Kdim,
         int Ndim, int n_nb, int act_rows) {
-    __shared__ __attribute__((aligned(1024))) u16 lds[2 * SELEMS];
+    __shared__ __attribute__((aligned(1024))) u16 lds[NTB * TELEMS + NWB * WELEMS];
 
     // Work item -> (expert, n-block, m-tile). Blocks are dispatched to the 8 XCDs round-robin
     // (block b on XCD b % 8); XCD x takes the contiguous item range [x*per_xcd, (x+1)*per_xcd),
@@ -224,20 +255,21 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(
     }
 
     // This wave's part of the tile: tokens 128*(wave % 2) .. +128, and four 16-row weight
-    // subtiles (gate/up: 32 gate rows and the matching 32 up rows; down: 64 rows).
+    // subtiles (gate/up: 32 gate rows and the matching 32 up rows; down: 64 rows), as rows
+    // of a weight buffer.
     const int wm = wave & 1, wn = wave >> 1;
     const int tok0 = 128 * wm;
     int wrow[4], c0;
     if constexpr (MODE == 0) {
         c0 = n0 + 32 * wn;
-        wrow[0] = GM + 32 * wn;
-        wrow[1] = GM + 32 * wn + 16;
-        wrow[2] = GM + GN / 2 + 32 * wn;
-        wrow[3] = GM + GN / 2 + 32 * wn + 16;
+        wrow[0] = 32 * wn;
+        wrow[1] = 32 * wn + 16;
+        wrow[2] = GN / 2 + 32 * wn;
+        wrow[3] = GN / 2 + 32 * wn + 16;
     } else {
         c0 = n0 + 64 * wn;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) wrow[q] = GM + 64 * wn + 16 * q;
+        for (int q = 0; q < 4; ++q) wrow[q] = 64 * wn + 16 * q;
     }
     const int real = rows - tok0;                   // real tokens in this wave's half (may be <= 0)
     const int live = real <= 0 ? 0 : min(8, 2 * ((real + 31) / 32));
