@@ -32,7 +32,7 @@ def _free_gpu():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("T", [1, 77, 129, 300])
+@pytest.mark.parametrize("T", [1, 33, 64, 77, 129, 300])
 def test_dense_mid_every_token(T):
     w = MID.with_T(T)
     print("case dense mid T", T, flush=True)
