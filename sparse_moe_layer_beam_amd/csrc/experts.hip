@@ -32,6 +32,12 @@ namespace {
 #ifndef BEAM_STREAM_NT
 #define BEAM_STREAM_NT 0        // 1: non-temporal weight loads
 #endif
+#ifndef BEAM_GU_KSPLIT
+#define BEAM_GU_KSPLIT 1        // gate/up: waves sharing one 16-channel group, each a part of k
+#endif
+#ifndef BEAM_DN_KSPLIT
+#define BEAM_DN_KSPLIT 2        // down: the same (2 measured 2% faster; gate/up measured slower split)
+#endif
 
 constexpr int kWavesPerBlock = 4;
 constexpr int kDgu = BEAM_GU_DEPTH;
@@ -104,27 +110,61 @@ __device__ __forceinline__ void zero_acc(f32x4 (&acc)[MT][1]) {
     for (int m = 0; m < MT; ++m) acc[m][0] = f32x4{0, 0, 0, 0};
 }
 
+// Sums the k-parts of a channel group: waves kp = 1..KS-1 of the group hand their partial
+// accumulators to wave kp = 0 through LDS, which adds them in kp order (a fixed order, so
+// the result does not depend on timing). Every wave of the block calls this.
+template <int KS, int MT, int NA>
+__device__ __forceinline__ void ksplit_reduce(f32x4 (&part)[kWavesPerBlock][NA][MT][64], int wave, int lane,
+                                              f32x4 (&a)[NA][MT][1]) {
+    if constexpr (KS > 1) {
+        const int kp = wave % KS;
+        if (kp != 0)
+#pragma unroll
+            for (int q = 0; q < NA; ++q)
+#pragma unroll
+                for (int m = 0; m < MT; ++m) part[wave][q][m][lane] = a[q][m][0];
+        __syncthreads();
+        if (kp == 0)
+#pragma unroll
+            for (int j = 1; j < KS; ++j)
+#pragma unroll
+                for (int q = 0; q < NA; ++q)
+#pragma unroll
+                    for (int m = 0; m < MT; ++m) {
+                        const f32x4 v = part[wave + j][q][m][lane];
+                        a[q][m][0] = f32x4{a[q][m][0][0] + v[0], a[q][m][0][1] + v[1], a[q][m][0][2] + v[2],
+                                           a[q][m][0][3] + v[3]};
+                    }
+    }
+}
+
 // h[beg+m, n] = bf16(silu(x_m . Wg[e,n]) * (x_m . Wu[e,n])) for the tokens m of expert e.
-// grid: (ceil(I / 64), E); block: 4 waves, each owning 16 output channels. A wave streams
-// its 16 gate rows, then its 16 up rows: one 16-row stream at a time keeps the number of
-// DRAM rows open across the chip low, which is what sets the achieved bandwidth here.
-// Three waves per SIMD with a 6-deep ring measured faster than two with 8 (same bytes in
-// flight, more streams to hide the stalls of each).
+// grid: (ceil(I / (16 * 4 / KS)), E); block: 4 waves. The KS waves of a 16-channel group
+// each stream a 1/KS part of k for those 16 gate rows, then the 16 up rows; their sums meet
+// in LDS. A wave streams one 16-row block at a time, which keeps the number of DRAM rows
+// open across the chip low, which is what sets the achieved bandwidth here. Splitting k
+// shortens each block, and with it the tail of the launch, where fewer and fewer blocks
+// are left to keep the memory busy. Three waves per SIMD with a 6-deep ring measured
+// faster than two with 8 (same bytes in flight, more streams to hide the stalls of each).
+template <int KS>
 __global__ __launch_bounds__(256, 3) void swiglu_stream_kernel(const u16* __restrict__ x,
                                                             const int32_t* __restrict__ offsets,
                                                             const int32_t* __restrict__ sorted_pairs, int K,
                                                             const u16* __restrict__ Wg, const u16* __restrict__ Wu,
                                                             u16* __restrict__ h, int d, int I) {
+    __shared__ f32x4 part[kWavesPerBlock][2][kMT][64];
     const int e = blockIdx.y;
     const int beg = offsets[e];
     const int n_e = offsets[e + 1] - beg;
     if (n_e <= 0) return;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int n0 = (blockIdx.x * kWavesPerBlock + wave) * 16;
-    if (n0 >= I) return;
-    const int r16 = lane & 15, kq = (lane >> 4) * 8;
-    const u16* const ag[1] = {Wg + ((size_t)e * I + n0 + r16) * d + kq};
-    const u16* const au[1] = {Wu + ((size_t)e * I + n0 + r16) * d + kq};
+    const int n0 = (blockIdx.x * (kWavesPerBlock / KS) + wave / KS) * 16;
+    const bool writer = wave % KS == 0 && n0 < I;
+    const int kl = d / KS;                                    // this wave's part of k
+    const int r16 = lane & 15, kq = (lane >> 4) * 8 + (wave % KS) * kl;
+    const int nr = min(n0, I - 16) + r16;                     // a group past I reads valid rows; discarded
+    const u16* const ag[1] = {Wg + ((size_t)e * I + nr) * d + kq};
+    const u16* const au[1] = {Wu + ((size_t)e * I + nr) * d + kq};
     for (int mb = 0; mb < n_e; mb += 16 * kMT) {
         const int ntile = min(kMT, (n_e - mb + 15) / 16);
         const u16* xp[kMT];
@@ -133,62 +173,72 @@ __global__ __launch_bounds__(256, 3) void swiglu_stream_kernel(const u16* __rest
             const int m = min(mb + 16 * mt + r16, n_e - 1);   // rows past the end read a valid row; discarded
             xp[mt] = x + (size_t)(sorted_pairs[beg + m] / K) * d + kq;
         }
-        f32x4 g[kMT][1], u[kMT][1];
-        zero_acc<kMT>(g);
-        zero_acc<kMT>(u);
-        stream_core<1, kMT, kDgu, kNT>(ag, xp, d, g);
-        stream_core<1, kMT, kDgu, kNT>(au, xp, d, u);
+        f32x4 gu[2][kMT][1];
+        zero_acc<kMT>(gu[0]);
+        zero_acc<kMT>(gu[1]);
+        stream_core<1, kMT, kDgu, kNT>(ag, xp, kl, gu[0]);
+        stream_core<1, kMT, kDgu, kNT>(au, xp, kl, gu[1]);
+        ksplit_reduce<KS, kMT, 2>(part, wave, lane, gu);
         // lane holds channels n0 + 4*(lane/16) + i for token row mb + 16*mt + lane%16
+        if (writer)
 #pragma unroll
-        for (int mt = 0; mt < kMT; ++mt) {
-            const int m = mb + 16 * mt + r16;
-            if (mt >= ntile || m >= n_e) continue;
-            const int n = n0 + (lane >> 4) * 4;
-            const f32x4 gv = g[mt][0], uv = u[mt][0];
-            uint32_t lo = (uint32_t)f32_to_bf16(silu_mul(gv[0], uv[0])) |
-                          ((uint32_t)f32_to_bf16(silu_mul(gv[1], uv[1])) << 16);
-            uint32_t hi = (uint32_t)f32_to_bf16(silu_mul(gv[2], uv[2])) |
-                          ((uint32_t)f32_to_bf16(silu_mul(gv[3], uv[3])) << 16);
-            *reinterpret_cast<uint2*>(h + (size_t)(beg + m) * I + n) = make_uint2(lo, hi);
-        }
+            for (int mt = 0; mt < kMT; ++mt) {
+                const int m = mb + 16 * mt + r16;
+                if (mt >= ntile || m >= n_e) continue;
+                const int n = n0 + (lane >> 4) * 4;
+                const f32x4 gv = gu[0][mt][0], uv = gu[1][mt][0];
+                uint32_t lo = (uint32_t)f32_to_bf16(silu_mul(gv[0], uv[0])) |
+                              ((uint32_t)f32_to_bf16(silu_mul(gv[1], uv[1])) << 16);
+                uint32_t hi = (uint32_t)f32_to_bf16(silu_mul(gv[2], uv[2])) |
+                              ((uint32_t)f32_to_bf16(silu_mul(gv[3], uv[3])) << 16);
+                *reinterpret_cast<uint2*>(h + (size_t)(beg + m) * I + n) = make_uint2(lo, hi);
+            }
+        if constexpr (KS > 1) __syncthreads();                // part is reused by the next token tile
     }
 }
 
 // y_perm[beg+m, c] = w_pair * (h[beg+m] . Wd[e,c]) for the tokens m of expert e.
-// grid: (ceil(d / 64), E); block: 4 waves, each streaming 16 rows of Wd.
+// grid: (ceil(d / (16 * 4 / KS)), E); block: 4 waves; the KS waves of a 16-row group of Wd
+// each stream a 1/KS part of k, as in the gate/up kernel.
+template <int KS>
 __global__ __launch_bounds__(256) void down_stream_kernel(const u16* __restrict__ h,
                                                           const int32_t* __restrict__ offsets,
                                                           const int32_t* __restrict__ sorted_pairs,
                                                           const float* __restrict__ topk_w,
                                                           const u16* __restrict__ Wd, float* __restrict__ y_perm,
                                                           int d, int I) {
+    __shared__ f32x4 part[kWavesPerBlock][1][kMT][64];
     const int e = blockIdx.y;
     const int beg = offsets[e];
     const int n_e = offsets[e + 1] - beg;
     if (n_e <= 0) return;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int n0 = (blockIdx.x * kWavesPerBlock + wave) * 16;
-    if (n0 >= d) return;
-    const int r16 = lane & 15, kq = (lane >> 4) * 8;
-    const u16* const a[1] = {Wd + ((size_t)e * d + n0 + r16) * I + kq};
+    const int n0 = (blockIdx.x * (kWavesPerBlock / KS) + wave / KS) * 16;
+    const bool writer = wave % KS == 0 && n0 < d;
+    const int kl = I / KS;
+    const int r16 = lane & 15, kq = (lane >> 4) * 8 + (wave % KS) * kl;
+    const u16* const a[1] = {Wd + ((size_t)e * d + min(n0, d - 16) + r16) * I + kq};
     for (int mb = 0; mb < n_e; mb += 16 * kMT) {
         const int ntile = min(kMT, (n_e - mb + 15) / 16);
         const u16* hp[kMT];
 #pragma unroll
         for (int mt = 0; mt < kMT; ++mt) hp[mt] = h + (size_t)(beg + min(mb + 16 * mt + r16, n_e - 1)) * I + kq;
-        f32x4 acc[kMT][1];
-        zero_acc<kMT>(acc);
-        stream_core<1, kMT, kDdn, kNT>(a, hp, I, acc);
+        f32x4 acc[1][kMT][1];
+        zero_acc<kMT>(acc[0]);
+        stream_core<1, kMT, kDdn, kNT>(a, hp, kl, acc[0]);
+        ksplit_reduce<KS, kMT, 1>(part, wave, lane, acc);
+        if (writer)
 #pragma unroll
-        for (int mt = 0; mt < kMT; ++mt) {
-            const int m = mb + 16 * mt + r16;
-            if (mt >= ntile || m >= n_e) continue;
-            const float wt = topk_w[sorted_pairs[beg + m]];
-            const int c = n0 + (lane >> 4) * 4;
-            const f32x4 v = acc[mt][0];
-            *reinterpret_cast<float4*>(y_perm + (size_t)(beg + m) * d + c) =
-                make_float4(wt * v[0], wt * v[1], wt * v[2], wt * v[3]);
-        }
+            for (int mt = 0; mt < kMT; ++mt) {
+                const int m = mb + 16 * mt + r16;
+                if (mt >= ntile || m >= n_e) continue;
+                const float wt = topk_w[sorted_pairs[beg + m]];
+                const int c = n0 + (lane >> 4) * 4;
+                const f32x4 v = acc[0][mt][0];
+                *reinterpret_cast<float4*>(y_perm + (size_t)(beg + m) * d + c) =
+                    make_float4(wt * v[0], wt * v[1], wt * v[2], wt * v[3]);
+            }
+        if constexpr (KS > 1) __syncthreads();
     }
 }
 
@@ -230,10 +280,16 @@ void launch_swiglu(const Shape& s, const void* x, const int32_t* offsets, const 
         launch_gemm_swiglu(s, x, offsets, sorted_pairs, tiles, n_tiles, Wg, Wu, h, st);
         return;
     }
-    const int per_block = kWavesPerBlock * 16;
-    hipLaunchKernelGGL(swiglu_stream_kernel, dim3((unsigned)((s.I + per_block - 1) / per_block), (unsigned)s.E),
-                       dim3(256), 0, st, (const u16*)x, offsets, sorted_pairs, s.K, (const u16*)Wg, (const u16*)Wu,
-                       (u16*)h, s.d, s.I);
+    // k parts must be whole 32-wide MFMA steps
+    const int ks = s.d % (32 * BEAM_GU_KSPLIT) == 0 ? BEAM_GU_KSPLIT : 1;
+    const int per_block = kWavesPerBlock / ks * 16;
+    const dim3 grid((unsigned)((s.I + per_block - 1) / per_block), (unsigned)s.E);
+    if (ks == BEAM_GU_KSPLIT)
+        hipLaunchKernelGGL(swiglu_stream_kernel<BEAM_GU_KSPLIT>, grid, dim3(256), 0, st, (const u16*)x, offsets,
+                           sorted_pairs, s.K, (const u16*)Wg, (const u16*)Wu, (u16*)h, s.d, s.I);
+    else
+        hipLaunchKernelGGL(swiglu_stream_kernel<1>, grid, dim3(256), 0, st, (const u16*)x, offsets, sorted_pairs, s.K,
+                           (const u16*)Wg, (const u16*)Wu, (u16*)h, s.d, s.I);
 }
 
 void launch_down(const Shape& s, const void* h, const int32_t* offsets, const int32_t* sorted_pairs,
@@ -243,10 +299,15 @@ void launch_down(const Shape& s, const void* h, const int32_t* offsets, const in
         launch_gemm_down(s, h, offsets, sorted_pairs, topk_w, tiles, n_tiles, Wd, y_perm, st);
         return;
     }
-    const int per_block = kWavesPerBlock * 16;
-    hipLaunchKernelGGL(down_stream_kernel, dim3((unsigned)((s.d + per_block - 1) / per_block), (unsigned)s.E),
-                       dim3(256), 0, st, (const u16*)h, offsets, sorted_pairs, topk_w, (const u16*)Wd, y_perm, s.d,
-                       s.I);
+    const int ks = s.I % (32 * BEAM_DN_KSPLIT) == 0 ? BEAM_DN_KSPLIT : 1;
+    const int per_block = kWavesPerBlock / ks * 16;
+    const dim3 grid((unsigned)((s.d + per_block - 1) / per_block), (unsigned)s.E);
+    if (ks == BEAM_DN_KSPLIT)
+        hipLaunchKernelGGL(down_stream_kernel<BEAM_DN_KSPLIT>, grid, dim3(256), 0, st, (const u16*)h, offsets,
+                           sorted_pairs, topk_w, (const u16*)Wd, y_perm, s.d, s.I);
+    else
+        hipLaunchKernelGGL(down_stream_kernel<1>, grid, dim3(256), 0, st, (const u16*)h, offsets, sorted_pairs, topk_w,
+                           (const u16*)Wd, y_perm, s.d, s.I);
 }
 
 void launch_combine(const Shape& s, const float* y_perm, const int32_t* pair_rank, float* y, hipStream_t st) {
