@@ -44,6 +44,7 @@ def lib():
         L.oracle_dispatch.argtypes = [vp, i64, i32, vp, vp, vp]
         L.oracle_expert.argtypes = [vp, i64, vp, vp, vp, i32, i32, vp, i32]
         L.oracle_moe_rows.argtypes = [vp, i64, vp, vp, i32, vp, vp, vp, i32, i32, vp, i32]
+        L.oracle_moe_share_rows.argtypes = [vp, i64, vp, vp, i32, i32, i32, vp, vp, vp, i32, i32, vp, i32]
         L.oracle_post_norm.argtypes = [vp, vp, i64, i32, dbl, vp, i32]
         L.oracle_residual_step.argtypes = [vp, vp, i64, i32, vp]
         L.oracle_contribution_index.argtypes = [i32, i32]
@@ -165,6 +166,32 @@ def moe_rows(x_rows, idx, w, experts, E: int) -> np.ndarray:
     y = np.empty((n, d), dtype=np.float64)
     lib().oracle_moe_rows(x_rows.ctypes.data, n, idx.ctypes.data, w.ctypes.data, K, ptrs[0], ptrs[1], ptrs[2],
                           d, I, y.ctypes.data, nthreads())
+    return y
+
+
+def moe_share_rows(x_rows, idx, w, experts, e_begin: int, e_count: int) -> np.ndarray:
+    """Expert-parallel share: the part of the layer output from experts [e_begin, e_begin+e_count)
+    ("Use HF Transformers" cookbook, Parallelism). experts maps global id -> (Wg[e], Wu[e], Wd[e])
+    and needs only the ids in the range that idx uses."""
+    x_rows = _c(x_rows, np.uint16)
+    idx = _c(idx, np.int32)
+    w = _c(w, np.float64)
+    n, d = x_rows.shape
+    K = idx.shape[1]
+    keep = []
+    ptrs = [(ctypes.c_void_p * max(1, e_count))() for _ in range(3)]
+    I = 1
+    for e in np.unique(idx):
+        if not (e_begin <= int(e) < e_begin + e_count):
+            continue
+        mats = [_c(a, np.uint16) for a in experts[int(e)]]
+        keep.append(mats)
+        I = mats[0].shape[0]
+        for k in range(3):
+            ptrs[k][int(e) - e_begin] = mats[k].ctypes.data
+    y = np.empty((n, d), dtype=np.float64)
+    lib().oracle_moe_share_rows(x_rows.ctypes.data, n, idx.ctypes.data, w.ctypes.data, K, e_begin, e_count, ptrs[0],
+                                ptrs[1], ptrs[2], d, I, y.ctypes.data, nthreads())
     return y
 
 

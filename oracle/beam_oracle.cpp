@@ -25,6 +25,9 @@
 //      archdb fact sheet, FFN rows];
 //   * y = sum of the weighted expert outputs, no shared expert [archdb fact sheet,
 //     MoE: always-on experts = 0].
+//   * expert-parallel share (optional): the same sum restricted to the slots whose expert
+//     lies in one contiguous block of expert ids, what one GPU computes when each holds a
+//     block of the experts ["Use HF Transformers" cookbook, Parallelism].
 //   * after the layer (next step on the path, optional): the post-MLP half of the
 //     sandwich norm on y, then the depth-scaled residual add, the k-th contribution
 //     entering as r * sqrt((k-1)/k) + n / sqrt(k), where the embedding counts as the
@@ -285,6 +288,35 @@ void oracle_moe_rows(const uint16_t* x_rows, int64_t n, const int32_t* idx, cons
         }
 }
 
+
+// Expert-parallel share ("Use HF Transformers" cookbook, Parallelism: each GPU holds a
+// contiguous block of the experts and computes the tokens routed to them): the part of
+// the layer output that experts [e_begin, e_begin + e_count) contribute,
+// y_part[i] = sum over slots j with idx[i,j] in that range, in slot order, of
+// w[i,j] * expert(x_i). Slots outside the range add nothing; a row with none is 0.
+// wg/wu/wd are indexed by the local id idx - e_begin. Summed over a partition of the
+// experts into such ranges, the shares give the whole layer output.
+void oracle_moe_share_rows(const uint16_t* x_rows, int64_t n, const int32_t* idx, const double* w, int32_t K,
+                           int32_t e_begin, int32_t e_count, const uint16_t* const* wg, const uint16_t* const* wu,
+                           const uint16_t* const* wd, int32_t d, int32_t I, double* y_out, int32_t nthreads) {
+    auto local = [&](int64_t q) {
+        const int e = idx[q] - e_begin;
+        return (e >= 0 && e < e_count) ? e : -1;
+    };
+    int64_t work = n * K;
+    std::vector<double> o((size_t)work * d, 0.0);
+    parallel_for(work, nthreads, [&](int64_t q) {
+        const int e = local(q);
+        if (e >= 0) expert_token(x_rows + (q / K) * d, wg[e], wu[e], wd[e], d, I, o.data() + q * d);
+    });
+    for (int64_t i = 0; i < n; ++i)
+        for (int c = 0; c < d; ++c) {
+            double acc = 0.0;
+            for (int j = 0; j < K; ++j)
+                if (local(i * K + j) >= 0) acc += w[i * K + j] * o[(i * K + j) * d + c];
+            y_out[i * d + c] = acc;
+        }
+}
 
 // Post-MLP RMSNorm of the layer output y [T,d] (double, unrounded): n[t,j] = y[t,j] * r_t * w[j],
 // r_t = 1 / sqrt(mean_j y[t,j]^2 + eps).

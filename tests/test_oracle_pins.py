@@ -298,6 +298,41 @@ def test_layer_invariants_tiny():
         np.testing.assert_allclose(y1[t], acc, rtol=0, atol=1e-13 * np.abs(acc).max())
 
 
+
+def test_expert_share_partitions_the_layer():
+    """Expert-parallel shares ("Use HF Transformers" cookbook, Parallelism): over any partition
+    of the experts into contiguous blocks the shares add up to the layer; the whole range is the
+    layer itself; a one-expert share is that expert's weighted output on the rows that chose it
+    and exactly 0 elsewhere; checked per token against torch float64 experts."""
+    w = recipes.WORKLOADS[0]
+    x = synth.hidden(w)
+    Wr = synth.router_weight(w)
+    b = synth.bias(w)
+    idx, wt, _ = oracle.route(x, Wr, b, w.n_group, w.topk_group, w.top_k, w.scale)
+    experts = {e: synth.expert_weights(w, e) for e in range(w.E)}
+    y = oracle.moe_rows(x, idx, wt, experts, w.E)
+    assert np.array_equal(oracle.moe_share_rows(x, idx, wt, experts, 0, w.E), y)
+    gs = w.E // w.n_group
+    for blocks in ([(g * gs, gs) for g in range(w.n_group)], [(0, 5), (5, 1), (6, w.E - 6)]):
+        tot = sum(oracle.moe_share_rows(x, idx, wt, experts, e0, n) for e0, n in blocks)
+        np.testing.assert_allclose(tot, y, rtol=0, atol=1e-13 * np.abs(y).max())
+    e1 = int(idx[3, 2])
+    one = oracle.moe_share_rows(x, idx, wt, experts, e1, 1)
+    for t in range(w.T):
+        hit = np.nonzero(idx[t] == e1)[0]
+        if len(hit) == 0:
+            assert np.all(one[t] == 0.0)
+        else:
+            exp = wt[t, hit[0]] * oracle.expert(x[t:t + 1], *experts[e1])[0]
+            assert np.array_equal(one[t], exp)
+    g0 = oracle.moe_share_rows(x, idx, wt, experts, 0, gs)
+    for t in (0, 3, 77):
+        ref = np.zeros(w.d)
+        for j in range(w.top_k):
+            if idx[t, j] < gs:
+                ref += wt[t, j] * _expert_torch(x[t:t + 1], *experts[int(idx[t, j])])[0][0]
+        np.testing.assert_allclose(g0[t], ref, rtol=0, atol=1e-12 * max(1.0, np.abs(ref).max()))
+
 # --- RMSNorm ------------------------------------------------------------------------------
 
 def test_rmsnorm_matches_torch_float64():
