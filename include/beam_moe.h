@@ -200,6 +200,35 @@ size_t beam_moe_dense_workspace_bytes(int64_t T, int32_t d, int32_t I);
 beam_moe_status beam_moe_dense_mlp(int64_t T, int32_t d, int32_t I, const void* x, const void* Wg, const void* Wu,
                                    const void* Wd, float* y, void* workspace, size_t ws_bytes, void* stream);
 
+/* Expert-parallel share of the layer: what one GPU computes when each GPU holds one
+ * contiguous block of the experts and the tokens routed to them are sent to it ("Use HF
+ * Transformers" cookbook, Parallelism: 32 of the 256 experts per GPU, which is one
+ * routing group). Given the routing of T tokens (from beam_moe_route on any device),
+ *   y_part[t] = sum over the slots j with e_begin <= topk_idx[t,j] < e_begin + e_count,
+ *               in slot order, of topk_w[t,j] * expert(x_t)
+ * (a row with no such slot is 0); summed over a partition of the experts into blocks, the
+ * shares give beam_moe_forward's y up to FP32 rounding order. Same kernels as the layer,
+ * on the local block only: dispatch of the local pairs, grouped SwiGLU GEMMs, combine.
+ *   shape      the model shape (E = all experts; its routing fields are only validated)
+ *              with T = number of tokens passed in
+ *   e_begin, e_count  the local block of expert ids: 1 <= e_count, 0 <= e_begin,
+ *              e_begin + e_count <= E, else BEAM_MOE_ERR_INVALID_ARG
+ *   x          [T, d] bf16 (the normed hidden states if the layer uses the norm)
+ *   topk_idx   [T, top_k] int32 global expert ids, distinct within a token; topk_w [T, top_k] FP32
+ *   Wg, Wu     [e_count, I, d] bf16, Wd [e_count, d, I] bf16: the local experts, local id
+ *              e - e_begin
+ *   y_part     [T, d] FP32 out, fully overwritten
+ *   workspace  at least beam_moe_share_workspace_bytes(shape, e_count) bytes
+ *   stage_events  NULL, or 6 hipEvent_t recorded as in beam_moe_forward_staged ([0] and
+ *              [1] together: there is no router step)
+ * All pointers 16-byte aligned. T = 0 returns BEAM_MOE_OK with no launch.
+ * beam_moe_share_workspace_bytes returns 0 for an invalid shape or e_count. */
+size_t beam_moe_share_workspace_bytes(const beam_moe_shape* shape, int32_t e_count);
+beam_moe_status beam_moe_experts_share(const beam_moe_shape* shape, int32_t e_begin, int32_t e_count, const void* x,
+                                       const int32_t* topk_idx, const float* topk_w, const void* Wg, const void* Wu,
+                                       const void* Wd, float* y_part, void* workspace, size_t ws_bytes, void* stream,
+                                       void* const* stage_events);
+
 /* Static, human-readable name of a status code. */
 const char* beam_moe_status_string(beam_moe_status status);
 

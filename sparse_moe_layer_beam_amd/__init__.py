@@ -22,7 +22,8 @@ BEAM_MOE_ERR_HIP = 4
 EXPORTED = ("beam_moe_workspace_bytes", "beam_moe_route", "beam_moe_dispatch", "beam_moe_forward",
             "beam_moe_forward_staged", "beam_moe_post_residual", "beam_moe_forward_residual",
             "beam_moe_dense_workspace_bytes", "beam_moe_dense_mlp", "beam_moe_quantize_fp8",
-            "beam_moe_forward_fp8", "beam_moe_status_string")
+            "beam_moe_forward_fp8", "beam_moe_share_workspace_bytes", "beam_moe_experts_share",
+            "beam_moe_status_string")
 N_STAGE_EVENTS = 6
 
 
@@ -83,6 +84,10 @@ def lib() -> ctypes.CDLL:
         L.beam_moe_quantize_fp8.restype = i32
         L.beam_moe_forward_fp8.argtypes = [shp] + [vp] * 14 + [sz, vp, vp]
         L.beam_moe_forward_fp8.restype = i32
+        L.beam_moe_share_workspace_bytes.argtypes = [shp, i32]
+        L.beam_moe_share_workspace_bytes.restype = sz
+        L.beam_moe_experts_share.argtypes = [shp, i32, i32] + [vp] * 7 + [vp, sz, vp, vp]
+        L.beam_moe_experts_share.restype = i32
         L.beam_moe_status_string.argtypes = [i32]
         L.beam_moe_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -208,3 +213,15 @@ def beam_moe_forward_fp8(shape, x, norm_w, Wr, bias, Wg8, Wu8, Wd8, sg, su, sd, 
                                     _ptr(topk_w), _ptr(logits), _ptr(workspace), _nbytes(workspace),
                                     _stream(stream), _events(stage_events))
     return _check(st, "beam_moe_forward_fp8") if check else st
+
+
+def beam_moe_share_workspace_bytes(shape, e_count: int) -> int:
+    return int(lib().beam_moe_share_workspace_bytes(ctypes.byref(shape), int(e_count)))
+
+
+def beam_moe_experts_share(shape, e_begin, e_count, x, topk_idx, topk_w, Wg, Wu, Wd, y_part, workspace,
+                           stage_events=None, stream=None, check=True) -> int:
+    st = lib().beam_moe_experts_share(ctypes.byref(shape), int(e_begin), int(e_count), _ptr(x), _ptr(topk_idx),
+                                      _ptr(topk_w), _ptr(Wg), _ptr(Wu), _ptr(Wd), _ptr(y_part), _ptr(workspace),
+                                      _nbytes(workspace), _stream(stream), _events(stage_events))
+    return _check(st, "beam_moe_experts_share") if check else st

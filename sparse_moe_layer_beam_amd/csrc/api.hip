@@ -323,6 +323,60 @@ beam_moe_status beam_moe_dense_mlp(int64_t T, int32_t d, int32_t I, const void* 
     return hip_status();
 }
 
+size_t beam_moe_share_workspace_bytes(const beam_moe_shape* shape, int32_t e_count) {
+    Shape s;
+    if (to_shape(shape, &s) != BEAM_MOE_OK || e_count < 1 || e_count > s.E) return 0;
+    Shape sl = s;
+    sl.E = e_count;
+    return layout(sl).total;
+}
+
+beam_moe_status beam_moe_experts_share(const beam_moe_shape* shape, int32_t e_begin, int32_t e_count, const void* x,
+                                       const int32_t* topk_idx, const float* topk_w, const void* Wg, const void* Wu,
+                                       const void* Wd, float* y_part, void* workspace, size_t ws_bytes, void* stream,
+                                       void* const* stage_events) {
+    Shape s;
+    beam_moe_status st = to_shape(shape, &s);
+    if (st != BEAM_MOE_OK) return st;
+    if (e_count < 1 || e_begin < 0 || e_begin > s.E - e_count) return BEAM_MOE_ERR_INVALID_ARG;
+    if (!x || !topk_idx || !topk_w || !Wg || !Wu || !Wd || !y_part) return BEAM_MOE_ERR_INVALID_ARG;
+    if (!aligned(x) || !aligned(topk_idx) || !aligned(topk_w) || !aligned(Wg) || !aligned(Wu) || !aligned(Wd) ||
+        !aligned(y_part))
+        return BEAM_MOE_ERR_INVALID_ARG;
+    if (s.T == 0) return BEAM_MOE_OK;
+    Shape sl = s;                 // the local experts are the whole expert set of this call
+    sl.E = e_count;
+    const Layout L = layout(sl);
+    if (!workspace || !aligned(workspace)) return BEAM_MOE_ERR_INVALID_ARG;
+    if (ws_bytes < L.total) return BEAM_MOE_ERR_WORKSPACE_TOO_SMALL;
+    hipStream_t hs = (hipStream_t)stream;
+    (void)hipGetLastError();
+    auto mark = [&](int i) {
+        if (stage_events && stage_events[i]) (void)hipEventRecord((hipEvent_t)stage_events[i], hs);
+    };
+    int32_t* idl = at<int32_t>(workspace, L.idx);
+    int32_t* off = at<int32_t>(workspace, L.off);
+    int32_t* sp = at<int32_t>(workspace, L.sp);
+    int32_t* pr = at<int32_t>(workspace, L.pr);
+    int32_t* tiles = at<int32_t>(workspace, L.tiles);
+    int32_t* ntiles = at<int32_t>(workspace, L.ntiles);
+    void* h = at<void>(workspace, L.h);
+    float* yp = at<float>(workspace, L.yp);
+    mark(0);
+    mark(1);
+    beam::launch_share_idx(topk_idx, s.T * s.K, e_begin, e_count, idl, hs);
+    beam::launch_dispatch(sl, idl, off, sp, pr, at<int32_t>(workspace, L.cc), at<int32_t>(workspace, L.ric), tiles,
+                          ntiles, beam::experts_tile_m(sl), hs);
+    mark(2);
+    beam::launch_swiglu(sl, x, off, sp, tiles, ntiles, Wg, Wu, h, hs);
+    mark(3);
+    beam::launch_down(sl, h, off, sp, topk_w, tiles, ntiles, Wd, yp, hs);
+    mark(4);
+    beam::launch_combine(sl, yp, pr, y_part, hs);
+    mark(5);
+    return hip_status();
+}
+
 const char* beam_moe_status_string(beam_moe_status status) {
     switch (status) {
         case BEAM_MOE_OK: return "ok";

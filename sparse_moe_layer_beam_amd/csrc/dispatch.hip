@@ -212,7 +212,22 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(const int32_t* __
     if (p >= offsets[E]) sorted_pairs[p] = -1;
 }
 
+// Expert-parallel share: global expert ids in [e_begin, e_begin + e_count) become local ids
+// 0..e_count-1, every other id -1 (the dispatch then leaves that pair out).
+__global__ __launch_bounds__(256) void share_idx_kernel(const int32_t* __restrict__ idx, int64_t P, int e_begin,
+                                                        int e_count, int32_t* __restrict__ idx_local) {
+    const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (p >= P) return;
+    const int e = idx[p] - e_begin;
+    idx_local[p] = (e >= 0 && e < e_count) ? e : -1;
+}
+
 }  // namespace
+
+void launch_share_idx(const int32_t* idx, int64_t P, int e_begin, int e_count, int32_t* idx_local, hipStream_t st) {
+    hipLaunchKernelGGL(share_idx_kernel, dim3((unsigned)((P + 255) / 256)), dim3(256), 0, st, idx, P, e_begin, e_count,
+                       idx_local);
+}
 
 void launch_dispatch(const Shape& s, const int32_t* idx, int32_t* offsets, int32_t* sorted_pairs, int32_t* pair_rank,
                      int32_t* chunk_counts, int32_t* rank_in_chunk, int32_t* tiles, int32_t* n_tiles, int tile_m,

@@ -242,8 +242,9 @@ __global__ __launch_bounds__(256) void down_stream_kernel(const u16* __restrict_
     }
 }
 
-// y[t] = sum over slots j = 0..K-1, in that order, of y_perm[pair_rank[t*K + j]].
-// grid: (T, ceil(d / 1024)); each thread owns one float4 of the row.
+// y[t] = sum over slots j = 0..K-1, in that order, of y_perm[pair_rank[t*K + j]]; slots with
+// pair_rank -1 (an expert this call does not hold: expert-parallel share) add nothing, and a
+// row with no slot left is 0. grid: (T, ceil(d / 1024)); each thread owns one float4 of the row.
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y_perm,
                                                       const int32_t* __restrict__ pair_rank, int K, int d,
                                                       float* __restrict__ y) {
@@ -252,15 +253,20 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     if (c >= d) return;
     int rk[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) rk[j] = j < K ? pair_rank[t * K + j] : 0;
+    for (int j = 0; j < 16; ++j) rk[j] = j < K ? pair_rank[t * K + j] : -1;
     float4 v[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j)
-        if (j < K) v[j] = *reinterpret_cast<const float4*>(y_perm + (size_t)rk[j] * d + c);
-    float4 acc = v[0];
+        if (rk[j] >= 0) v[j] = *reinterpret_cast<const float4*>(y_perm + (size_t)rk[j] * d + c);
+    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    bool first = true;
 #pragma unroll
-    for (int j = 1; j < 16; ++j)
-        if (j < K) { acc.x += v[j].x; acc.y += v[j].y; acc.z += v[j].z; acc.w += v[j].w; }
+    for (int j = 0; j < 16; ++j)
+        if (rk[j] >= 0) {
+            if (first) acc = v[j];
+            else { acc.x += v[j].x; acc.y += v[j].y; acc.z += v[j].z; acc.w += v[j].w; }
+            first = false;
+        }
     *reinterpret_cast<float4*>(y + t * d + c) = acc;
 }
 

@@ -48,6 +48,9 @@ void launch_down(const Shape& s, const void* h, const int32_t* offsets, const in
                  hipStream_t st);
 void launch_combine(const Shape& s, const float* y_perm, const int32_t* pair_rank, float* y, hipStream_t st);
 
+// Expert ids -> local ids of the block [e_begin, e_begin + e_count), -1 outside (expert-parallel share).
+void launch_share_idx(const int32_t* idx, int64_t P, int e_begin, int e_count, int32_t* idx_local, hipStream_t st);
+
 // FP8 (OCP E4M3 + one E8M0 scale per 32 values) expert weights for decode (experts_fp8.hip).
 void launch_fp8_quantize(int64_t rows, int K, const void* w, void* q, void* s, hipStream_t st);
 bool fp8_supports(const Shape& s);

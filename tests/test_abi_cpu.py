@@ -209,6 +209,38 @@ def test_fp8_entry_points_validate_before_launching():
     assert f(odd, A, None, A, A, A, A, A, A, A, A, A, None, None, None, WS(n)) == UNSUPPORTED
 
 
+
+def test_expert_share_validates_before_launching():
+    s = beam()
+    n = moe.beam_moe_share_workspace_bytes(s, 32)
+    assert 0 < n < moe.beam_moe_workspace_bytes(s)
+    assert moe.beam_moe_share_workspace_bytes(s, 0) == 0
+    assert moe.beam_moe_share_workspace_bytes(s, 257) == 0
+
+    class WS:
+        def __init__(self, nbytes):
+            self.n = nbytes
+
+        def data_ptr(self):
+            return A
+
+        def numel(self):
+            return self.n
+
+        def element_size(self):
+            return 1
+
+    f = lambda sh, e0, ne, *a: moe.beam_moe_experts_share(sh, e0, ne, *a, stream=0, check=False)
+    # args: x, idx, w, Wg, Wu, Wd, y_part, ws
+    assert f(s, 0, 32, A, A, A, A, A, A, A, WS(n - 1)) == WS_SMALL
+    assert f(s, 224, 33, A, A, A, A, A, A, A, WS(n)) == INVALID       # block past the last expert
+    assert f(s, -1, 32, A, A, A, A, A, A, A, WS(n)) == INVALID
+    assert f(s, 0, 0, A, A, A, A, A, A, A, WS(n)) == INVALID
+    assert f(s, 0, 32, A, None, A, A, A, A, A, WS(n)) == INVALID      # topk_idx missing
+    assert f(s, 0, 32, A, A, A, A, A, A, A + 8, WS(n)) == INVALID     # misaligned y_part
+    assert f(beam(d=5120 + 32), 0, 32, A, A, A, A, A, A, A, WS(n)) == UNSUPPORTED
+    assert f(beam(T=0), 0, 32, A, A, A, A, A, A, A, None) == OK
+
 def test_zero_tokens_returns_ok_without_workspace():
     s = beam(T=0)
     assert moe.beam_moe_forward(s, A, None, A, A, A, A, A, A, None, None, None, None, stream=0, check=False) == OK
