@@ -58,7 +58,16 @@ typedef struct beam_moe_shape {
     float routed_scaling_factor;  /* 2.5 */
     int32_t norm_topk_prob;       /* 1: renormalise the chosen weights to sum to 1 first */
     float rms_eps;                /* 1e-6; used only when a norm weight is given */
+    int32_t weight_layout;        /* BEAM_MOE_WEIGHTS_ROW_MAJOR (0) or BEAM_MOE_WEIGHTS_PACKED (1) */
 } beam_moe_shape;
+
+/* Layout of the expert weights Wg, Wu [E, I, d] and Wd [E, d, I] that a call reads.
+ * ROW_MAJOR: as written, row-major. PACKED: the same bf16 values rearranged by
+ * beam_moe_pack_weights, once, when the weights are loaded; every entry point that takes a
+ * shape and bf16 expert weights accepts either (beam_moe_forward_fp8 only ROW_MAJOR: FP8
+ * weights have their own layout), with bitwise-identical results. Packed, the decode
+ * weight streams read whole contiguous kilobytes and run ~10% faster on MI355X. */
+enum { BEAM_MOE_WEIGHTS_ROW_MAJOR = 0, BEAM_MOE_WEIGHTS_PACKED = 1 };
 
 typedef enum beam_moe_status {
     BEAM_MOE_OK = 0,
@@ -228,6 +237,17 @@ beam_moe_status beam_moe_experts_share(const beam_moe_shape* shape, int32_t e_be
                                        const int32_t* topk_idx, const float* topk_w, const void* Wg, const void* Wu,
                                        const void* Wd, float* y_part, void* workspace, size_t ws_bytes, void* stream,
                                        void* const* stage_events);
+
+/* Rearranges a bf16 weight matrix w [rows, K] (row-major) into the PACKED layout of the
+ * expert weights: rows in blocks of 16; block b is a run of K/32 steps of 512 values, step
+ * j holding, for lane l = 0..63, the 8 values w[16b + l % 16][32j + 8(l / 16) .. +8] (the
+ * operand a wave of 64 lanes feeds one 16x16x32 MFMA). Pack Wg and Wu as [E*I, d] and Wd
+ * as [E*d, I]; the expert blocks stay contiguous (expert e is rows [e*I, (e+1)*I)), so a
+ * slice of experts of a packed tensor is the packed tensor of those experts.
+ *   rows     a multiple of 16;  K  a multiple of 32  (else BEAM_MOE_ERR_INVALID_ARG)
+ *   w        [rows, K] bf16 in;  packed  [rows * K] bf16 out, not overlapping w
+ * Pointers 16-byte aligned; rows * K below 2^40. rows = 0 returns BEAM_MOE_OK. */
+beam_moe_status beam_moe_pack_weights(int64_t rows, int32_t K, const void* w, void* packed, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* beam_moe_status_string(beam_moe_status status);

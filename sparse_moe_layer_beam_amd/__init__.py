@@ -23,7 +23,7 @@ EXPORTED = ("beam_moe_workspace_bytes", "beam_moe_route", "beam_moe_dispatch", "
             "beam_moe_forward_staged", "beam_moe_post_residual", "beam_moe_forward_residual",
             "beam_moe_dense_workspace_bytes", "beam_moe_dense_mlp", "beam_moe_quantize_fp8",
             "beam_moe_forward_fp8", "beam_moe_share_workspace_bytes", "beam_moe_experts_share",
-            "beam_moe_status_string")
+            "beam_moe_pack_weights", "beam_moe_status_string")
 N_STAGE_EVENTS = 6
 
 
@@ -39,6 +39,7 @@ class beam_moe_shape(ctypes.Structure):
         ("routed_scaling_factor", ctypes.c_float),
         ("norm_topk_prob", ctypes.c_int32),
         ("rms_eps", ctypes.c_float),
+        ("weight_layout", ctypes.c_int32),
     ]
 
 
@@ -88,16 +89,22 @@ def lib() -> ctypes.CDLL:
         L.beam_moe_share_workspace_bytes.restype = sz
         L.beam_moe_experts_share.argtypes = [shp, i32, i32] + [vp] * 7 + [vp, sz, vp, vp]
         L.beam_moe_experts_share.restype = i32
+        L.beam_moe_pack_weights.argtypes = [ctypes.c_int64, i32, vp, vp, vp]
+        L.beam_moe_pack_weights.restype = i32
         L.beam_moe_status_string.argtypes = [i32]
         L.beam_moe_status_string.restype = ctypes.c_char_p
         _lib = L
     return _lib
 
 
+WEIGHTS_ROW_MAJOR, WEIGHTS_PACKED = 0, 1
+
+
 def make_shape(T, d, E, n_group, topk_group, top_k, I, routed_scaling_factor=2.5, norm_topk_prob=True,
-               rms_eps=1e-6) -> beam_moe_shape:
+               rms_eps=1e-6, weight_layout=WEIGHTS_ROW_MAJOR) -> beam_moe_shape:
     return beam_moe_shape(int(T), int(d), int(E), int(n_group), int(topk_group), int(top_k), int(I),
-                          float(routed_scaling_factor), int(bool(norm_topk_prob)), float(rms_eps))
+                          float(routed_scaling_factor), int(bool(norm_topk_prob)), float(rms_eps),
+                          int(weight_layout))
 
 
 def _ptr(t):
@@ -225,3 +232,18 @@ def beam_moe_experts_share(shape, e_begin, e_count, x, topk_idx, topk_w, Wg, Wu,
                                       _ptr(topk_w), _ptr(Wg), _ptr(Wu), _ptr(Wd), _ptr(y_part), _ptr(workspace),
                                       _nbytes(workspace), _stream(stream), _events(stage_events))
     return _check(st, "beam_moe_experts_share") if check else st
+
+
+def beam_moe_pack_weights(rows, K, w, packed, stream=None, check=True) -> int:
+    st = lib().beam_moe_pack_weights(int(rows), int(K), _ptr(w), _ptr(packed), _stream(stream))
+    return _check(st, "beam_moe_pack_weights") if check else st
+
+
+def pack_expert_weights(Wg, Wu, Wd, stream=None):
+    """Packed copies of the expert weights (torch tensors [E, I, d], [E, I, d], [E, d, I])."""
+    out = []
+    for w in (Wg, Wu, Wd):
+        p = w.new_empty(w.shape)
+        beam_moe_pack_weights(w.shape[0] * w.shape[1], w.shape[2], w, p, stream)
+        out.append(p)
+    return tuple(out)

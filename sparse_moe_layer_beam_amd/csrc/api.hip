@@ -31,8 +31,11 @@ beam_moe_status to_shape(const beam_moe_shape* p, Shape* s) {
     }
     if (gsz % epl || !pow2(gsz / epl)) return BEAM_MOE_ERR_UNSUPPORTED_SHAPE;
     if (p->T * (int64_t)p->top_k >= (int64_t)INT32_MAX) return BEAM_MOE_ERR_UNSUPPORTED_SHAPE;
+    if (p->weight_layout != BEAM_MOE_WEIGHTS_ROW_MAJOR && p->weight_layout != BEAM_MOE_WEIGHTS_PACKED)
+        return BEAM_MOE_ERR_INVALID_ARG;
     s->T = p->T; s->d = p->d; s->E = p->E; s->G = p->n_group; s->KG = p->topk_group; s->K = p->top_k; s->I = p->I;
     s->S = p->routed_scaling_factor; s->norm = p->norm_topk_prob ? 1 : 0; s->eps = p->rms_eps;
+    s->packed = p->weight_layout == BEAM_MOE_WEIGHTS_PACKED ? 1 : 0;
     return BEAM_MOE_OK;
 }
 
@@ -155,7 +158,7 @@ beam_moe_status check_fp8(const Shape& s, const Fp8& f) {
     if (!f.Wg || !f.Wu || !f.Wd || !f.sg || !f.su || !f.sd) return BEAM_MOE_ERR_INVALID_ARG;
     if (!aligned(f.Wg) || !aligned(f.Wu) || !aligned(f.Wd) || !aligned(f.sg) || !aligned(f.su) || !aligned(f.sd))
         return BEAM_MOE_ERR_INVALID_ARG;
-    if (!beam::fp8_supports(s)) return BEAM_MOE_ERR_UNSUPPORTED_SHAPE;
+    if (!beam::fp8_supports(s) || s.packed) return BEAM_MOE_ERR_UNSUPPORTED_SHAPE;
     return BEAM_MOE_OK;
 }
 
@@ -374,6 +377,16 @@ beam_moe_status beam_moe_experts_share(const beam_moe_shape* shape, int32_t e_be
     mark(4);
     beam::launch_combine(sl, yp, pr, y_part, hs);
     mark(5);
+    return hip_status();
+}
+
+beam_moe_status beam_moe_pack_weights(int64_t rows, int32_t K, const void* w, void* packed, void* stream) {
+    if (rows < 0 || rows % 16 != 0 || K <= 0 || K % 32 != 0) return BEAM_MOE_ERR_INVALID_ARG;
+    if (!w || !packed || !aligned(w) || !aligned(packed) || w == packed) return BEAM_MOE_ERR_INVALID_ARG;
+    if (rows * (int64_t)K >= ((int64_t)1 << 40)) return BEAM_MOE_ERR_UNSUPPORTED_SHAPE;
+    if (rows == 0) return BEAM_MOE_OK;
+    (void)hipGetLastError();
+    beam::launch_pack_stream(w, packed, rows, K, (hipStream_t)stream);
     return hip_status();
 }
 

@@ -50,12 +50,12 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 typedef __attribute__((address_space(3))) void lds_void;
 
 // Direct loads of this wave's 64 rows of stage s into buffer buf (token waves: a token
-// buffer; weight waves: a weight buffer): load i fills rows 8i .. +8 of the wave's part
-// (1 KB, 1 KB aligned), lane l writing 16 bytes at l*16.
-__device__ __forceinline__ void stage_load(const u16* const (&src)[DMA], int s, u16* buf) {
+// buffer; weight waves: a weight buffer): load i fills 1 KB of the wave's part (1 KB
+// aligned), lane l writing 16 bytes at l*16; src[i] + s*step is this lane's source.
+__device__ __forceinline__ void stage_load(const u16* const (&src)[DMA], int s, int step, u16* buf) {
 #pragma unroll
     for (int i = 0; i < DMA; ++i)
-        __builtin_amdgcn_global_load_lds((const void*)(src[i] + s * GK), (lds_void*)(buf + 8 * i * GK), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(src[i] + s * step), (lds_void*)(buf + 8 * i * GK), 16, 0, 0);
 }
 
 // End of a stage: this wave's loads that the next stage needs have landed and its LDS reads
@@ -71,8 +71,8 @@ __device__ __forceinline__ void stage_end(bool deep) {
 // One stage: MFMAs of the wave's LIVE 16-token subtiles against its four 16-row weight
 // subtiles, k = 64, from token buffer tb and weight buffer wb. Fragment of global k-chunk
 // c (8 bf16) of a buffer row r sits at r*64 + 8*(c ^ (r % 8)); this lane's rows all have
-// r % 8 == lane % 8.
-template <int LIVE>
+// r % 8 == lane % 8. Packed weights arrive in fragment order instead (PK).
+template <int LIVE, bool PK>
 __device__ __forceinline__ void stage_mma(const u16* tb, const u16* wb, int tok0, const int (&wrow)[4], int lane,
                                           f32x4 (&acc)[8][4]) {
     const int lr = lane & 15, sw = lane & 7, c0 = lane >> 4;
@@ -80,8 +80,12 @@ __device__ __forceinline__ void stage_mma(const u16* tb, const u16* wb, int tok0
     for (int j = 0; j < 2; ++j) {
         const int pos = ((4 * j + c0) ^ sw) * 8;
         bf16x8 w[4];
+        // packed weights: 16-row block b, k-step j of the stage is the 1 KB at b*1024 + j*512,
+        // already in fragment order
 #pragma unroll
-        for (int q = 0; q < 4; ++q) w[q] = *reinterpret_cast<const bf16x8*>(wb + (wrow[q] + lr) * GK + pos);
+        for (int q = 0; q < 4; ++q)
+            w[q] = PK ? *reinterpret_cast<const bf16x8*>(wb + (wrow[q] / 16) * 1024 + j * 512 + lane * 8)
+                      : *reinterpret_cast<const bf16x8*>(wb + (wrow[q] + lr) * GK + pos);
         if constexpr (LIVE > 0) {
             bf16x8 xr[kFrag];
 #pragma unroll
@@ -102,7 +106,7 @@ __device__ __forceinline__ void stage_mma(const u16* tb, const u16* wb, int tok0
 }
 
 // K loop and epilogue for a wave whose first LIVE 16-token subtiles hold real tokens.
-template <int MODE, int LIVE>
+template <int MODE, int LIVE, bool PK>
 __device__ __forceinline__ void gemm_run(u16* lds, const u16* const (&src)[DMA], int nstages, int wave, int lane,
                                          int tok0, const int (&wrow)[4], int rows, size_t orow0, int c0, int Ndim,
                                          const int32_t* __restrict__ pair_of_row, const float* __restrict__ topk_w,
@@ -127,14 +131,16 @@ __device__ __forceinline__ void gemm_run(u16* lds, const u16* const (&src)[DMA],
     u16* const mine = (weight_wave ? wbuf : tbuf) + part;
     const int belems = weight_wave ? WELEMS : TELEMS;
     const bool deep = nb == 3;
-    stage_load(src, 0, mine);
-    if (deep) stage_load(src, min(1, last), mine + belems);
+    // source elements per stage: 64 k of a row-major row; packed, two 32-k steps of 512
+    const int step = (PK && weight_wave) ? 1024 : GK;
+    stage_load(src, 0, step, mine);
+    if (deep) stage_load(src, min(1, last), step, mine + belems);
     stage_end(deep);
     for (int s = 0; s < nstages; ++s) {
         // the buffer loaded here was last read in stage s-1, which every wave has left
         const int ahead = nb - 1;
-        stage_load(src, min(s + ahead, last), mine + ((s + ahead) % nb) * belems);
-        stage_mma<LIVE>(tbuf + (s % NTB) * TELEMS, wbuf + (s % NWB) * WELEMS, tok0, wrow, lane, acc);
+        stage_load(src, min(s + ahead, last), step, mine + ((s + ahead) % nb) * belems);
+        stage_mma<LIVE, PK>(tbuf + (s % NTB) * TELEMS, wbuf + (s % NWB) * WELEMS, tok0, wrow, lane, acc);
         stage_end(deep);
     }
     // the weight waves' last (clamped, unused) loads must land before the block's LDS is released
@@ -181,7 +187,7 @@ __device__ __forceinline__ void gemm_run(u16* lds, const u16* const (&src)[DMA],
 //         W0 = Wd [E, Ndim, Kdim].
 // DENSE: one expert holding all act_rows tokens in order (the dense SwiGLU MLP): no tile
 //         list, no gather, weight 1; MODE 1 then writes y [T, d] directly.
-template <int MODE, bool DENSE>
+template <int MODE, bool DENSE, bool PK>
 __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(
         const u16* __restrict__ act, const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pairs,
         const int32_t* __restrict__ tiles, const int32_t* __restrict__ n_tiles_p, const u16* __restrict__ W0,
@@ -249,6 +255,20 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(
             if constexpr (MODE == 0 && !DENSE) tr = (size_t)(sorted_pairs[beg + m] / top_k);
             else tr = (size_t)(beg + m);
             p = act + tr * Kdim;
+        } else if constexpr (PK) {
+            // weight wave ww loads 16-row blocks 4ww .. 4ww+3 of the tile, two 32-k steps each
+            const int qb = 4 * (wave - NW / 2) + i / 2;
+            int ch;
+            const u16* W = W0;
+            if constexpr (MODE == 0) {
+                ch = n0 + 16 * (qb % (GN / 32));
+                if (qb >= GN / 32) W = W1;
+            } else {
+                ch = n0 + 16 * qb;
+            }
+            const size_t blk = ((size_t)e * Ndim + min(ch, Ndim - 16)) / 16;   // past Ndim: the last block
+            src[i] = W + (blk * (Kdim / 32) * 64 + lane) * 8 + (i % 2) * 512;
+            continue;
         } else {
             const int wr = row - GM;
             int ch;
@@ -293,8 +313,8 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(
     switch (live) {
 #define BEAM_GEMM_CASE(L)                                                                                     \
     case L:                                                                                                   \
-        gemm_run<MODE, L>(lds, src, nstages, wave, lane, tok0, wrow, rows, orow0, c0, Ndim, pair_of_row,      \
-                          topk_w, out);                                                                       \
+        gemm_run<MODE, L, PK>(lds, src, nstages, wave, lane, tok0, wrow, rows, orow0, c0, Ndim, pair_of_row,  \
+                              topk_w, out);                                                                   \
         break;
         BEAM_GEMM_CASE(0) BEAM_GEMM_CASE(2) BEAM_GEMM_CASE(4) BEAM_GEMM_CASE(6) BEAM_GEMM_CASE(8)
 #undef BEAM_GEMM_CASE
@@ -320,9 +340,12 @@ void launch_gemm_swiglu(const Shape& s, const void* x, const int32_t* offsets, c
                         hipStream_t st) {
     const int n_nb = (s.I + GN / 2 - 1) / (GN / 2);
     const int blocks = (max_items(s, n_nb) + 7) / 8 * 8;
-    hipLaunchKernelGGL((grouped_gemm_kernel<0, false>), dim3((unsigned)blocks), dim3(NT), 0, st, (const u16*)x, offsets,
-                       sorted_pairs, tiles, n_tiles, (const u16*)Wg, (const u16*)Wu, nullptr, s.K, h, s.d, s.I,
-                       n_nb, (int)s.T);
+#define BEAM_GU(PK)                                                                                           \
+    hipLaunchKernelGGL((grouped_gemm_kernel<0, false, PK>), dim3((unsigned)blocks), dim3(NT), 0, st,           \
+                       (const u16*)x, offsets, sorted_pairs, tiles, n_tiles, (const u16*)Wg, (const u16*)Wu,  \
+                       nullptr, s.K, h, s.d, s.I, n_nb, (int)s.T)
+    if (s.packed) BEAM_GU(true); else BEAM_GU(false);
+#undef BEAM_GU
 }
 
 void launch_gemm_down(const Shape& s, const void* h, const int32_t* offsets, const int32_t* sorted_pairs,
@@ -330,9 +353,12 @@ void launch_gemm_down(const Shape& s, const void* h, const int32_t* offsets, con
                       float* y_perm, hipStream_t st) {
     const int n_nb = (s.d + GN - 1) / GN;
     const int blocks = (max_items(s, n_nb) + 7) / 8 * 8;
-    hipLaunchKernelGGL((grouped_gemm_kernel<1, false>), dim3((unsigned)blocks), dim3(NT), 0, st, (const u16*)h, offsets,
-                       sorted_pairs, tiles, n_tiles, (const u16*)Wd, nullptr, topk_w, s.K, y_perm, s.I, s.d,
-                       n_nb, (int)(s.T * s.K));
+#define BEAM_DN(PK)                                                                                           \
+    hipLaunchKernelGGL((grouped_gemm_kernel<1, false, PK>), dim3((unsigned)blocks), dim3(NT), 0, st,           \
+                       (const u16*)h, offsets, sorted_pairs, tiles, n_tiles, (const u16*)Wd, nullptr, topk_w, \
+                       s.K, y_perm, s.I, s.d, n_nb, (int)(s.T * s.K))
+    if (s.packed) BEAM_DN(true); else BEAM_DN(false);
+#undef BEAM_DN
 }
 
 // Dense SwiGLU MLP (one expert, all T tokens in order): h = bf16(silu(x . Wg^T) * (x . Wu^T)),
@@ -341,7 +367,7 @@ void launch_dense_swiglu(int64_t T, int d, int I, const void* x, const void* Wg,
                          hipStream_t st) {
     const int n_nb = (I + GN / 2 - 1) / (GN / 2);
     const int items = (int)((T + GM - 1) / GM) * n_nb;
-    hipLaunchKernelGGL((grouped_gemm_kernel<0, true>), dim3((unsigned)((items + 7) / 8 * 8)), dim3(NT), 0, st,
+    hipLaunchKernelGGL((grouped_gemm_kernel<0, true, false>), dim3((unsigned)((items + 7) / 8 * 8)), dim3(NT), 0, st,
                        (const u16*)x, nullptr, nullptr, nullptr, nullptr, (const u16*)Wg, (const u16*)Wu, nullptr, 1,
                        h, d, I, n_nb, (int)T);
 }
@@ -349,7 +375,7 @@ void launch_dense_swiglu(int64_t T, int d, int I, const void* x, const void* Wg,
 void launch_dense_down(int64_t T, int d, int I, const void* h, const void* Wd, float* y, hipStream_t st) {
     const int n_nb = (d + GN - 1) / GN;
     const int items = (int)((T + GM - 1) / GM) * n_nb;
-    hipLaunchKernelGGL((grouped_gemm_kernel<1, true>), dim3((unsigned)((items + 7) / 8 * 8)), dim3(NT), 0, st,
+    hipLaunchKernelGGL((grouped_gemm_kernel<1, true, false>), dim3((unsigned)((items + 7) / 8 * 8)), dim3(NT), 0, st,
                        (const u16*)h, nullptr, nullptr, nullptr, nullptr, (const u16*)Wd, nullptr, nullptr, 1, y, I, d,
                        n_nb, (int)T);
 }

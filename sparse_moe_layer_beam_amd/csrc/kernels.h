@@ -12,6 +12,7 @@ struct Shape {
     float S;
     int norm;
     float eps;
+    int packed;     // expert weights in the packed layout of beam_moe_pack_weights
 };
 
 // Router (router.hip)
@@ -47,6 +48,9 @@ void launch_down(const Shape& s, const void* h, const int32_t* offsets, const in
                  const float* topk_w, const int32_t* tiles, const int32_t* n_tiles, const void* Wd, float* y_perm,
                  hipStream_t st);
 void launch_combine(const Shape& s, const float* y_perm, const int32_t* pair_rank, float* y, hipStream_t st);
+
+// Weights [rows, K] -> the packed layout of beam_moe_pack_weights (rows % 16 == 0, K % 32 == 0).
+void launch_pack_stream(const void* W, void* P, int64_t rows, int K, hipStream_t st);
 
 // Expert ids -> local ids of the block [e_begin, e_begin + e_count), -1 outside (expert-parallel share).
 void launch_share_idx(const int32_t* idx, int64_t P, int e_begin, int e_count, int32_t* idx_local, hipStream_t st);

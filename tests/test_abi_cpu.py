@@ -42,6 +42,10 @@ def test_shape_struct_matches_header_layout():
     assert ctypes.sizeof(moe.beam_moe_shape) == 48
     assert moe.beam_moe_shape.routed_scaling_factor.offset == 32
     assert moe.beam_moe_shape.rms_eps.offset == 40
+    assert moe.beam_moe_shape.weight_layout.offset == 44
+    text = open(HEADER).read()
+    assert "BEAM_MOE_WEIGHTS_ROW_MAJOR = 0" in text and "BEAM_MOE_WEIGHTS_PACKED = 1" in text
+    assert (moe.WEIGHTS_ROW_MAJOR, moe.WEIGHTS_PACKED) == (0, 1)
 
 
 def beam(T=64, **kw):
@@ -66,6 +70,9 @@ def beam(T=64, **kw):
     (dict(E=256, n_group=128, topk_group=4), UNSUPPORTED),   # more than 64 groups
     (dict(E=24, n_group=4, topk_group=2, top_k=4), UNSUPPORTED),  # 6 lanes per group
     (dict(T=1 << 28), UNSUPPORTED),    # T * top_k overflows int32 pair ids
+    (dict(weight_layout=1), OK),
+    (dict(weight_layout=2), INVALID),
+    (dict(weight_layout=-1), INVALID),
 ])
 def test_shape_validation(kw, status):
     s = beam(**kw)
@@ -240,6 +247,36 @@ def test_expert_share_validates_before_launching():
     assert f(s, 0, 32, A, A, A, A, A, A, A + 8, WS(n)) == INVALID     # misaligned y_part
     assert f(beam(d=5120 + 32), 0, 32, A, A, A, A, A, A, A, WS(n)) == UNSUPPORTED
     assert f(beam(T=0), 0, 32, A, A, A, A, A, A, A, None) == OK
+
+
+def test_pack_weights_validates_before_launching():
+    f = lambda *a: moe.beam_moe_pack_weights(*a, stream=0, check=False)
+    assert f(24, 64, A, A + (1 << 20)) == INVALID          # rows not a multiple of 16
+    assert f(32, 48, A, A + (1 << 20)) == INVALID          # K not a multiple of 32
+    assert f(32, 64, A, A) == INVALID                      # in place
+    assert f(32, 64, A + 2, A + (1 << 20)) == INVALID      # misaligned
+    assert f(32, 64, None, A) == INVALID
+    assert f(-16, 64, A, A + (1 << 20)) == INVALID
+    assert f(1 << 36, 1 << 10, A, A + (1 << 20)) == UNSUPPORTED
+    assert f(0, 64, A, A + (1 << 20)) == OK
+
+
+def test_fp8_rejects_the_packed_bf16_layout():
+    s = beam(weight_layout=1)
+    n = moe.beam_moe_workspace_bytes(s)
+
+    class WS:
+        def data_ptr(self):
+            return A
+
+        def numel(self):
+            return n
+
+        def element_size(self):
+            return 1
+
+    f = lambda sh, *a: moe.beam_moe_forward_fp8(sh, *a, stream=0, check=False)
+    assert f(s, A, None, A, A, A, A, A, A, A, A, A, None, None, None, WS()) == UNSUPPORTED
 
 def test_zero_tokens_returns_ok_without_workspace():
     s = beam(T=0)
