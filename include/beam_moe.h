@@ -64,9 +64,9 @@ typedef struct beam_moe_shape {
 /* Layout of the expert weights Wg, Wu [E, I, d] and Wd [E, d, I] that a call reads.
  * ROW_MAJOR: as written, row-major. PACKED: the same bf16 values rearranged by
  * beam_moe_pack_weights, once, when the weights are loaded; every entry point that takes a
- * shape and bf16 expert weights accepts either (beam_moe_forward_fp8 only ROW_MAJOR: FP8
- * weights have their own layout), with bitwise-identical results. Packed, the decode
- * weight streams read whole contiguous kilobytes and run ~10% faster on MI355X. */
+ * shape and expert weights accepts either (for FP8 weights, see beam_moe_forward_fp8), with
+ * bitwise-identical results. Packed, the decode weight streams read whole contiguous
+ * kilobytes and run ~10% faster on MI355X. */
 enum { BEAM_MOE_WEIGHTS_ROW_MAJOR = 0, BEAM_MOE_WEIGHTS_PACKED = 1 };
 
 typedef enum beam_moe_status {
@@ -187,7 +187,11 @@ beam_moe_status beam_moe_quantize_fp8(int64_t rows, int32_t K, const void* w, vo
  * [E, I, d], Wd8 [E, d, I], sg, su [E, I, d/32], sd [E, d, I/32]) and widen them exactly to bf16
  * in registers, so the result is the bf16 layer's on the dequantized weights. Decode-sized
  * batches only (T * top_k <= 16 * E) with d and I multiples of 512, else
- * BEAM_MOE_ERR_UNSUPPORTED_SHAPE. All pointers 16-byte aligned. */
+ * BEAM_MOE_ERR_UNSUPPORTED_SHAPE. All pointers 16-byte aligned.
+ * With weight_layout = BEAM_MOE_WEIGHTS_PACKED the codes are packed: each code matrix q
+ * [rows, K] passed through beam_moe_pack_weights(rows, K / 2, q, q_packed) (two codes per
+ * 16-bit unit), which gives 16-row blocks of 64-k steps of 1 KB; the scales stay as the
+ * quantizer wrote them. The result is bitwise the row-major one. */
 beam_moe_status beam_moe_forward_fp8(const beam_moe_shape* shape, const void* x, const void* norm_w, const float* Wr,
                                      const float* bias, const void* Wg8, const void* Wu8, const void* Wd8,
                                      const void* sg, const void* su, const void* sd, float* y, int32_t* topk_idx,

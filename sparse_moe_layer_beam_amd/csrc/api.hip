@@ -158,7 +158,7 @@ beam_moe_status check_fp8(const Shape& s, const Fp8& f) {
     if (!f.Wg || !f.Wu || !f.Wd || !f.sg || !f.su || !f.sd) return BEAM_MOE_ERR_INVALID_ARG;
     if (!aligned(f.Wg) || !aligned(f.Wu) || !aligned(f.Wd) || !aligned(f.sg) || !aligned(f.su) || !aligned(f.sd))
         return BEAM_MOE_ERR_INVALID_ARG;
-    if (!beam::fp8_supports(s) || s.packed) return BEAM_MOE_ERR_UNSUPPORTED_SHAPE;
+    if (!beam::fp8_supports(s)) return BEAM_MOE_ERR_UNSUPPORTED_SHAPE;
     return BEAM_MOE_OK;
 }
 

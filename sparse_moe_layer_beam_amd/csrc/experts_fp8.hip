@@ -5,7 +5,10 @@
 // conversion and scaled-MFMA instructions are built around.
 //
 // Weights are stored as q [rows, K] bytes and s [rows, K/32] bytes; a value is
-// 2^(s - 127) * e4m3(q). The kernels stream q from HBM (half the bytes of bf16), widen it
+// 2^(s - 127) * e4m3(q). The codes may instead be in the packed layout (beam_moe_pack_weights
+// on q viewed as [rows, K/2] 16-bit units): 16-row blocks of 64-k steps, each step the 1 KB
+// one wave loads (lane l: row l % 16, bytes 64t + 16(l / 16) .. +16), so every load is
+// contiguous; the scales stay row-major. The kernels stream q from HBM (half the bytes of bf16), widen it
 // to bf16 in registers with v_cvt_scalef32_pk_bf16_fp8 (exact: an E4M3 value times a power
 // of two has at most 4 significant bits) and run the same bf16 MFMAs with FP32
 // accumulation as the bf16 path, so the layer computes exactly the bf16 layer on the
@@ -108,10 +111,12 @@ __device__ __forceinline__ bf16x8 widen(uint32_t lo, uint32_t hi, float sc) {
 // at the decode workload it runs as fast as two passes (a second open row stream per wave
 // costs what the saved loads gain); with 1-byte weights the activation loads, not the
 // weights, hold these kernels below the bf16 kernels' share of HBM bandwidth.
-// wq[b]: row r of block b + 16c bytes; ws[b]: its scale bytes; x: token rows + 16c elements.
-template <int RB, int MT>
+// wq[b]: row r of block b + 16c bytes (packed: the lane's 16 bytes of step 0, steps 1 KB apart);
+// ws[b]: its scale bytes; x: token rows + 16c elements.
+template <int RB, int MT, bool PK>
 __device__ __forceinline__ void stream_fp8(const uint8_t* const (&wq)[RB], const uint8_t* const (&ws)[RB],
                                            const u16* const (&x)[MT], int K, int c, f32x4 (&acc)[MT][RB]) {
+    constexpr int kWB = PK ? 1024 : 64;                           // weight bytes from one step to the next
     u32x4 wa[kD][RB];
     bf16x8 xa[kD][MT][2];
     const int nsteps = K / 64;
@@ -125,7 +130,7 @@ __device__ __forceinline__ void stream_fp8(const uint8_t* const (&wq)[RB], const
 #pragma unroll
     for (int t = 0; t < kD; ++t) {
 #pragma unroll
-        for (int b = 0; b < RB; ++b) wa[t][b] = *reinterpret_cast<const u32x4*>(wq[b] + 64 * t);
+        for (int b = 0; b < RB; ++b) wa[t][b] = *reinterpret_cast<const u32x4*>(wq[b] + kWB * t);
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
             xa[t][m][0] = *reinterpret_cast<const bf16x8*>(x[m] + 64 * t);
@@ -151,9 +156,10 @@ __device__ __forceinline__ void stream_fp8(const uint8_t* const (&wq)[RB], const
                     acc[m][b] = mfma16(a1, xa[t][m][1], acc[m][b]);
                 }
             }
-            const int kn = 64 * min(g + kD + t, last);             // clamped: in bounds, unused at the end
+            const int tn = min(g + kD + t, last);                  // clamped: in bounds, unused at the end
+            const int kn = 64 * tn;
 #pragma unroll
-            for (int b = 0; b < RB; ++b) wa[t][b] = *reinterpret_cast<const u32x4*>(wq[b] + kn);
+            for (int b = 0; b < RB; ++b) wa[t][b] = *reinterpret_cast<const u32x4*>(wq[b] + (size_t)kWB * tn);
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
                 xa[t][m][0] = *reinterpret_cast<const bf16x8*>(x[m] + kn);
@@ -168,6 +174,7 @@ __device__ __forceinline__ void stream_fp8(const uint8_t* const (&wq)[RB], const
 // h[beg+m, n] = bf16(silu(x_m . Wg[e,n]) * (x_m . Wu[e,n])) for the tokens m of expert e, fp8
 // weights. grid: (ceil(I / 64), E); block: 4 waves of 16 output channels, each streaming its
 // gate and up rows together.
+template <bool PK>
 __global__ __launch_bounds__(256) void swiglu_fp8_kernel(const u16* __restrict__ x, const int32_t* __restrict__ offsets,
                                                          const int32_t* __restrict__ sorted_pairs, int top_k,
                                                          const uint8_t* __restrict__ Wg, const uint8_t* __restrict__ Wu,
@@ -185,10 +192,11 @@ __global__ __launch_bounds__(256) void swiglu_fp8_kernel(const u16* __restrict__
     for (int mb = 0; mb < n_e; mb += 16) {
         const int m = min(mb + r, n_e - 1);                         // rows past the end repeat a valid row
         const u16* const xp[1] = {x + (size_t)(sorted_pairs[beg + m] / top_k) * d + 16 * c};
-        const uint8_t* const wq[2] = {Wg + row * d + 16 * c, Wu + row * d + 16 * c};
+        const size_t wo = PK ? (((size_t)e * I + n0) / 16 * (d / 64) * 64 + lane) * 16 : row * d + 16 * c;
+        const uint8_t* const wq[2] = {Wg + wo, Wu + wo};
         const uint8_t* const ws[2] = {sg + row * (d / 32), su + row * (d / 32)};
         f32x4 acc[1][2] = {{{0, 0, 0, 0}, {0, 0, 0, 0}}};
-        stream_fp8<2, 1>(wq, ws, xp, d, c, acc);
+        stream_fp8<2, 1, PK>(wq, ws, xp, d, c, acc);
         const f32x4 g = acc[0][0], u = acc[0][1];
         // lane holds channels n0 + 4c + i of token mb + r
         if (mb + r < n_e) {
@@ -202,6 +210,7 @@ __global__ __launch_bounds__(256) void swiglu_fp8_kernel(const u16* __restrict__
 }
 
 // y_perm[beg+m, n] = w_pair * (h[beg+m] . Wd[e,n]) with fp8 Wd. grid: (ceil(d / 64), E).
+template <bool PK>
 __global__ __launch_bounds__(256) void down_fp8_kernel(const u16* __restrict__ h, const int32_t* __restrict__ offsets,
                                                        const int32_t* __restrict__ sorted_pairs,
                                                        const float* __restrict__ topk_w,
@@ -218,10 +227,11 @@ __global__ __launch_bounds__(256) void down_fp8_kernel(const u16* __restrict__ h
     const size_t row = (size_t)e * d + n0 + r;
     for (int mb = 0; mb < n_e; mb += 16) {
         const u16* const hp[1] = {h + (size_t)(beg + min(mb + r, n_e - 1)) * I + 16 * c};
-        const uint8_t* const wq[1] = {Wd + row * I + 16 * c};
+        const size_t wo = PK ? (((size_t)e * d + n0) / 16 * (I / 64) * 64 + lane) * 16 : row * I + 16 * c;
+        const uint8_t* const wq[1] = {Wd + wo};
         const uint8_t* const ws[1] = {sd + row * (I / 32)};
         f32x4 acc[1][1] = {{{0, 0, 0, 0}}};
-        stream_fp8<1, 1>(wq, ws, hp, I, c, acc);
+        stream_fp8<1, 1, PK>(wq, ws, hp, I, c, acc);
         if (mb + r < n_e) {
             const float wt = topk_w[sorted_pairs[beg + mb + r]];
             *reinterpret_cast<float4*>(y_perm + (size_t)(beg + mb + r) * d + n0 + 4 * c) =
@@ -242,17 +252,23 @@ bool fp8_supports(const Shape& s) { return s.d % 512 == 0 && s.I % 512 == 0 && !
 
 void launch_swiglu_fp8(const Shape& s, const void* x, const int32_t* offsets, const int32_t* sorted_pairs,
                        const void* Wg8, const void* Wu8, const void* sg, const void* su, void* h, hipStream_t st) {
-    hipLaunchKernelGGL(swiglu_fp8_kernel, dim3((unsigned)((s.I + 63) / 64), (unsigned)s.E), dim3(256), 0, st,
-                       static_cast<const u16*>(x), offsets, sorted_pairs, s.K, static_cast<const uint8_t*>(Wg8),
-                       static_cast<const uint8_t*>(Wu8), static_cast<const uint8_t*>(sg),
-                       static_cast<const uint8_t*>(su), static_cast<u16*>(h), s.d, s.I);
+#define BEAM_GU8(PK)                                                                                          \
+    hipLaunchKernelGGL((swiglu_fp8_kernel<PK>), dim3((unsigned)((s.I + 63) / 64), (unsigned)s.E), dim3(256), 0, st, \
+                       static_cast<const u16*>(x), offsets, sorted_pairs, s.K, static_cast<const uint8_t*>(Wg8),   \
+                       static_cast<const uint8_t*>(Wu8), static_cast<const uint8_t*>(sg),                         \
+                       static_cast<const uint8_t*>(su), static_cast<u16*>(h), s.d, s.I)
+    if (s.packed) BEAM_GU8(true); else BEAM_GU8(false);
+#undef BEAM_GU8
 }
 
 void launch_down_fp8(const Shape& s, const void* h, const int32_t* offsets, const int32_t* sorted_pairs,
                      const float* topk_w, const void* Wd8, const void* sd, float* y_perm, hipStream_t st) {
-    hipLaunchKernelGGL(down_fp8_kernel, dim3((unsigned)((s.d + 63) / 64), (unsigned)s.E), dim3(256), 0, st,
-                       static_cast<const u16*>(h), offsets, sorted_pairs, topk_w, static_cast<const uint8_t*>(Wd8),
-                       static_cast<const uint8_t*>(sd), y_perm, s.d, s.I);
+#define BEAM_DN8(PK)                                                                                          \
+    hipLaunchKernelGGL((down_fp8_kernel<PK>), dim3((unsigned)((s.d + 63) / 64), (unsigned)s.E), dim3(256), 0, st,   \
+                       static_cast<const u16*>(h), offsets, sorted_pairs, topk_w, static_cast<const uint8_t*>(Wd8), \
+                       static_cast<const uint8_t*>(sd), y_perm, s.d, s.I)
+    if (s.packed) BEAM_DN8(true); else BEAM_DN8(false);
+#undef BEAM_DN8
 }
 
 }  // namespace beam

@@ -261,22 +261,26 @@ def test_pack_weights_validates_before_launching():
     assert f(0, 64, A, A + (1 << 20)) == OK
 
 
-def test_fp8_rejects_the_packed_bf16_layout():
+def test_fp8_packed_layout_validates_like_row_major():
     s = beam(weight_layout=1)
     n = moe.beam_moe_workspace_bytes(s)
 
     class WS:
+        def __init__(self, nbytes):
+            self.n = nbytes
+
         def data_ptr(self):
             return A
 
         def numel(self):
-            return n
+            return self.n
 
         def element_size(self):
             return 1
 
     f = lambda sh, *a: moe.beam_moe_forward_fp8(sh, *a, stream=0, check=False)
-    assert f(s, A, None, A, A, A, A, A, A, A, A, A, None, None, None, WS()) == UNSUPPORTED
+    assert f(s, A, None, A, A, A, A, A, A, A, A, A, None, None, None, WS(n - 1)) == WS_SMALL
+    assert f(beam(T=8192, weight_layout=1), A, None, A, A, A, A, A, A, A, A, A, None, None, None, WS(n)) == UNSUPPORTED
 
 def test_zero_tokens_returns_ok_without_workspace():
     s = beam(T=0)

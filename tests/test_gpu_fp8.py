@@ -77,7 +77,19 @@ def _gpu_fp8_forward(w, t):
     y0 = torch.empty_like(y)
     moe.beam_moe_forward(shape, hid, t.get("norm_w"), t["Wr"], t["bias"], t["Wg"], t["Wu"], t["Wd"], y0, None, None,
                          None, ws)
+    # packed codes (two codes per 16-bit unit through beam_moe_pack_weights): bitwise the same layer
+    packed = []
+    for q, rows, K in ((qg, rows_gu, w.d), (qu, rows_gu, w.d), (qd, rows_d, w.I)):
+        p = torch.empty_like(q)
+        moe.beam_moe_pack_weights(rows, K // 2, q, p)
+        packed.append(p)
+    shape_pk = moe.make_shape(w.T, w.d, w.E, w.n_group, w.topk_group, w.top_k, w.I, w.scale, w.norm_topk_prob, w.eps,
+                              weight_layout=moe.WEIGHTS_PACKED)
+    y_pk = torch.full_like(y, float("nan"))
+    moe.beam_moe_forward_fp8(shape_pk, hid, t.get("norm_w"), t["Wr"], t["bias"], *packed, sg, su, sd, y_pk, None,
+                             None, None, ws)
     torch.cuda.synchronize()
+    assert torch.equal(y, y_pk), "packed fp8 codes changed the layer output"
     return y.cpu().numpy(), idx.cpu().numpy(), wt.cpu().numpy(), y0.cpu().numpy()
 
 
