@@ -202,16 +202,21 @@ beam_moe_status beam_moe_forward_fp8(const beam_moe_shape* shape, const void* x,
  * first 3 layers use a dense SwiGLU MLP; BeamConfig: intermediate_size, hidden_act):
  *   y = Wd . bf16(silu(Wg . x) * (Wu . x))   per token, BF16 MFMA with FP32 accumulation,
  * h rounded to bf16 once as in the experts; no routing, no scaling.
- *   T, d, I    tokens, hidden size (5120), intermediate size (20480); d and I multiples of
- *              128 with T*d, T*I and d*I below 2^31 (else BEAM_MOE_ERR_UNSUPPORTED_SHAPE)
+ *   T, d, I    tokens, hidden size (5120), intermediate size (20480). T <= 64 (decode): d and I
+ *              multiples of 64; weight streams against the tokens, the reduction over k split
+ *              in parts added in a fixed order. Larger T: the tiled GEMM, d and I multiples of
+ *              128. T*d, T*I and d*I below 2^31. Else BEAM_MOE_ERR_UNSUPPORTED_SHAPE.
+ *   weight_layout  BEAM_MOE_WEIGHTS_ROW_MAJOR, or PACKED (Wg, Wu through beam_moe_pack_weights
+ *              as [I, d], Wd as [d, I]); else BEAM_MOE_ERR_INVALID_ARG. Same results either way.
  *   x          [T, d] bf16
  *   Wg, Wu     [I, d] bf16;  Wd [d, I] bf16
  *   y          [T, d] FP32 out
- *   workspace  at least beam_moe_dense_workspace_bytes(T, d, I) bytes (holds h [T, I] bf16)
+ *   workspace  at least beam_moe_dense_workspace_bytes(T, d, I) bytes
  * T = 0 returns BEAM_MOE_OK with no launch. */
 size_t beam_moe_dense_workspace_bytes(int64_t T, int32_t d, int32_t I);
-beam_moe_status beam_moe_dense_mlp(int64_t T, int32_t d, int32_t I, const void* x, const void* Wg, const void* Wu,
-                                   const void* Wd, float* y, void* workspace, size_t ws_bytes, void* stream);
+beam_moe_status beam_moe_dense_mlp(int64_t T, int32_t d, int32_t I, int32_t weight_layout, const void* x,
+                                   const void* Wg, const void* Wu, const void* Wd, float* y, void* workspace,
+                                   size_t ws_bytes, void* stream);
 
 /* Expert-parallel share of the layer: what one GPU computes when each GPU holds one
  * contiguous block of the experts and the tokens routed to them are sent to it ("Use HF

@@ -79,7 +79,7 @@ def lib() -> ctypes.CDLL:
         L.beam_moe_forward_residual.restype = i32
         L.beam_moe_dense_workspace_bytes.argtypes = [ctypes.c_int64, i32, i32]
         L.beam_moe_dense_workspace_bytes.restype = sz
-        L.beam_moe_dense_mlp.argtypes = [ctypes.c_int64, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.beam_moe_dense_mlp.argtypes = [ctypes.c_int64, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
         L.beam_moe_dense_mlp.restype = i32
         L.beam_moe_quantize_fp8.argtypes = [ctypes.c_int64, i32, vp, vp, vp, vp]
         L.beam_moe_quantize_fp8.restype = i32
@@ -202,9 +202,10 @@ def beam_moe_dense_workspace_bytes(T: int, d: int, I: int) -> int:
     return int(lib().beam_moe_dense_workspace_bytes(int(T), int(d), int(I)))
 
 
-def beam_moe_dense_mlp(T, d, I, x, Wg, Wu, Wd, y, workspace, stream=None, check=True) -> int:
-    st = lib().beam_moe_dense_mlp(int(T), int(d), int(I), _ptr(x), _ptr(Wg), _ptr(Wu), _ptr(Wd), _ptr(y),
-                                  _ptr(workspace), _nbytes(workspace), _stream(stream))
+def beam_moe_dense_mlp(T, d, I, x, Wg, Wu, Wd, y, workspace, weight_layout=WEIGHTS_ROW_MAJOR, stream=None,
+                       check=True) -> int:
+    st = lib().beam_moe_dense_mlp(int(T), int(d), int(I), int(weight_layout), _ptr(x), _ptr(Wg), _ptr(Wu), _ptr(Wd),
+                                  _ptr(y), _ptr(workspace), _nbytes(workspace), _stream(stream))
     return _check(st, "beam_moe_dense_mlp") if check else st
 
 
@@ -245,5 +246,15 @@ def pack_expert_weights(Wg, Wu, Wd, stream=None):
     for w in (Wg, Wu, Wd):
         p = w.new_empty(w.shape)
         beam_moe_pack_weights(w.shape[0] * w.shape[1], w.shape[2], w, p, stream)
+        out.append(p)
+    return tuple(out)
+
+
+def pack_dense_weights(Wg, Wu, Wd, stream=None):
+    """Packed copies of the dense MLP weights (torch tensors [I, d], [I, d], [d, I])."""
+    out = []
+    for w in (Wg, Wu, Wd):
+        p = w.new_empty(w.shape)
+        beam_moe_pack_weights(w.shape[0], w.shape[1], w, p, stream)
         out.append(p)
     return tuple(out)

@@ -2,6 +2,7 @@
 // on the caller's stream. Contract and citations: include/beam_moe.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -307,22 +308,33 @@ beam_moe_status beam_moe_forward_fp8(const beam_moe_shape* shape, const void* x,
 
 size_t beam_moe_dense_workspace_bytes(int64_t T, int32_t d, int32_t I) {
     if (T < 0 || d <= 0 || I <= 0) return 0;
-    return up((size_t)T * (size_t)I * 2);
+    size_t n = up((size_t)T * (size_t)I * 2);
+    if (beam::dense_stream_supports(T, d, I)) n = std::max(n, beam::dense_stream_workspace_bytes(T, d, I));
+    return n;
 }
 
-beam_moe_status beam_moe_dense_mlp(int64_t T, int32_t d, int32_t I, const void* x, const void* Wg, const void* Wu,
-                                   const void* Wd, float* y, void* workspace, size_t ws_bytes, void* stream) {
+beam_moe_status beam_moe_dense_mlp(int64_t T, int32_t d, int32_t I, int32_t weight_layout, const void* x,
+                                   const void* Wg, const void* Wu, const void* Wd, float* y, void* workspace,
+                                   size_t ws_bytes, void* stream) {
     if (T < 0 || d <= 0 || I <= 0) return BEAM_MOE_ERR_INVALID_ARG;
+    if (weight_layout != BEAM_MOE_WEIGHTS_ROW_MAJOR && weight_layout != BEAM_MOE_WEIGHTS_PACKED)
+        return BEAM_MOE_ERR_INVALID_ARG;
     if (!x || !Wg || !Wu || !Wd || !y) return BEAM_MOE_ERR_INVALID_ARG;
     if (!aligned(x) || !aligned(Wg) || !aligned(Wu) || !aligned(Wd) || !aligned(y)) return BEAM_MOE_ERR_INVALID_ARG;
-    if (!beam::dense_supports(T, d, I)) return BEAM_MOE_ERR_UNSUPPORTED_SHAPE;
+    const bool stream_path = beam::dense_stream_supports(T, d, I);
+    if (!stream_path && !beam::dense_supports(T, d, I)) return BEAM_MOE_ERR_UNSUPPORTED_SHAPE;
     if (T == 0) return BEAM_MOE_OK;
     if (!workspace || !aligned(workspace)) return BEAM_MOE_ERR_INVALID_ARG;
     if (ws_bytes < beam_moe_dense_workspace_bytes(T, d, I)) return BEAM_MOE_ERR_WORKSPACE_TOO_SMALL;
     hipStream_t hs = (hipStream_t)stream;
+    const bool packed = weight_layout == BEAM_MOE_WEIGHTS_PACKED;
     (void)hipGetLastError();
-    beam::launch_dense_swiglu(T, d, I, x, Wg, Wu, workspace, hs);
-    beam::launch_dense_down(T, d, I, workspace, Wd, y, hs);
+    if (stream_path) {
+        beam::launch_dense_stream(T, d, I, packed, x, Wg, Wu, Wd, y, workspace, hs);
+    } else {
+        beam::launch_dense_swiglu(T, d, I, packed, x, Wg, Wu, workspace, hs);
+        beam::launch_dense_down(T, d, I, packed, workspace, Wd, y, hs);
+    }
     return hip_status();
 }
 

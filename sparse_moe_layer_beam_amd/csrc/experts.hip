@@ -68,12 +68,12 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 }
 
 // acc[m][r] += A_r . B_m^T over k in [0, K): A_r = 16 weight rows (lane: row r16, k-chunk kq),
-// B_m = 16 token rows. Weights and token fragments live in a ring of D register slots: slot s
+// B_m = 16 token rows (PK / PT: weights / token tiles in the packed layout). Weights and token fragments live in a ring of D register slots: slot s
 // is consumed by its MFMAs and then refilled with the step D ahead, so every wave keeps
 // D*(RB+MT) 16-byte loads in flight without register copies. Prefetch addresses past the end
 // are clamped to the last step (a redundant, in-bounds load that is never consumed); the
 // (K/32) % D leftover steps are taken from the ring after the main loop.
-template <int RB, int MT, int D, bool NT, bool PK>
+template <int RB, int MT, int D, bool NT, bool PK, bool PT = false>
 __device__ __forceinline__ void stream_core(const u16* const (&a)[RB], const u16* const (&b)[MT], int K,
                                             f32x4 (&acc)[MT][RB]) {
     bf16x8 wa[D][RB], xb[D][MT];
@@ -86,7 +86,7 @@ __device__ __forceinline__ void stream_core(const u16* const (&a)[RB], const u16
 #pragma unroll
         for (int r = 0; r < RB; ++r) wa[s][r] = ldw<NT>(a[r] + k * kWStep<PK>);
 #pragma unroll
-        for (int m = 0; m < MT; ++m) xb[s][m] = ld8(b[m] + k);
+        for (int m = 0; m < MT; ++m) xb[s][m] = ld8(b[m] + k * kWStep<PT>);
         if constexpr (BEAM_STREAM_PIN != 0) __builtin_amdgcn_sched_barrier(0);
     }
     for (int k0 = 0; k0 < kfull; k0 += 32 * D) {
@@ -100,7 +100,7 @@ __device__ __forceinline__ void stream_core(const u16* const (&a)[RB], const u16
 #pragma unroll
             for (int r = 0; r < RB; ++r) wa[s][r] = ldw<NT>(a[r] + kn * kWStep<PK>);
 #pragma unroll
-            for (int m = 0; m < MT; ++m) xb[s][m] = ld8(b[m] + kn);
+            for (int m = 0; m < MT; ++m) xb[s][m] = ld8(b[m] + kn * kWStep<PT>);
             if constexpr (BEAM_STREAM_PIN != 0) __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -290,22 +290,144 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     *reinterpret_cast<float4*>(y + t * d + c) = acc;
 }
 
-// Packed stream layout of a weight matrix W [rows, K] (rows % 16 == 0, K % 32 == 0): 16-row
-// blocks, each a run of K/32 steps of 64 lanes x 8 elements, lane l holding row l % 16,
-// k = 32 j + 8 (l / 16) .. +8 of step j: the order in which a streaming wave loads it, so every
-// 1 KB load is contiguous. One thread per 8 elements.
+// Packed layout of a matrix W [rows, K] (rows % 16 == 0, K % 32 == 0): 16-row blocks, each a
+// run of K/32 steps of 64 lanes x 8 elements, lane l holding row l % 16, k = 32 j + 8 (l / 16)
+// .. +8 of step j: the order in which a streaming wave loads it, so every 1 KB load is
+// contiguous. Rows at or past valid_rows repeat row valid_rows - 1 (token tiles padded to 16).
+// One thread per 8 elements.
 __global__ __launch_bounds__(256) void pack_stream_kernel(const u16* __restrict__ W, u16* __restrict__ P,
-                                                          int64_t rows, int K) {
+                                                          int64_t rows, int64_t valid_rows, int K) {
     const int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x;    // output chunk of 8 elements
     const int64_t steps = K / 32;
     if (o >= (rows / 16) * steps * 64) return;                     // rows * K / 8 chunks
     const int l = (int)(o & 63);
     const int64_t bj = o >> 6;
     const int64_t b = bj / steps, j = bj - b * steps;
-    const int64_t r = 16 * b + (l & 15);
+    const int64_t r = min(16 * b + (l & 15), valid_rows - 1);
     const int64_t k = 32 * j + 8 * (l >> 4);
     *reinterpret_cast<uint4*>(P + o * 8) = *reinterpret_cast<const uint4*>(W + r * K + k);
 }
+
+// ---- dense SwiGLU MLP, decode-sized batches (T <= 64) ------------------------------------
+// All T tokens are one expert; every weight byte must serve all of them in one pass. The
+// tokens go to packed 16-token tiles first (four tiles, padded with the last token), so each
+// wave's token fragments are contiguous kilobytes like its weight fragments; each wave streams
+// 16 weight rows over a 1/KS part of k against the four tiles, and the KS parts meet in a
+// fixed-order reduction that also applies the SwiGLU (gate/up) or writes y (down).
+constexpr int kDT = 4;                   // token tiles (64 tokens)
+constexpr int kDDgu = 3, kDDdn = 4;      // ring depths of the dense streams (gate/up holds both accumulators)
+
+// part[kb][0|1][t][n] = partial gate|up sums of channel n for token t over k-part kb.
+// grid: (I / 64, KS); block: 4 waves of 16 channels.
+template <bool PK>
+__global__ __launch_bounds__(256, 3) void dense_gu_stream_kernel(const u16* __restrict__ xp, const u16* __restrict__ Wg,
+                                                              const u16* __restrict__ Wu, float* __restrict__ part,
+                                                              int d, int I) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int n0 = (blockIdx.x * kWavesPerBlock + wave) * 16;
+    const int kb = blockIdx.y, kl = d / (int)gridDim.y, k0 = kb * kl;
+    const size_t wo = PK ? ((size_t)n0 / 16 * (d / 32) * 64 + lane) * 8 + (size_t)k0 * 16
+                         : (size_t)(n0 + (lane & 15)) * d + (lane >> 4) * 8 + k0;
+    const u16* const ag[1] = {Wg + wo};
+    const u16* const au[1] = {Wu + wo};
+    const u16* xb[kDT];
+#pragma unroll
+    for (int m = 0; m < kDT; ++m) xb[m] = xp + ((size_t)m * (d / 32) * 64 + lane) * 8 + (size_t)k0 * 16;
+    f32x4 g[kDT][1], u[kDT][1];
+    zero_acc<kDT>(g);
+    zero_acc<kDT>(u);
+    stream_core<1, kDT, kDDgu, kNT, PK, true>(ag, xb, kl, g);
+    stream_core<1, kDT, kDDgu, kNT, PK, true>(au, xb, kl, u);
+    // lane holds channels n0 + 4 (lane / 16) + i for token 16 m + lane % 16
+    const int tp = 16 * kDT;
+#pragma unroll
+    for (int m = 0; m < kDT; ++m) {
+        const size_t row = (size_t)(16 * m + (lane & 15)) * I + n0 + 4 * (lane >> 4);
+        *reinterpret_cast<f32x4*>(part + ((size_t)kb * 2 * tp) * I + row) = g[m][0];
+        *reinterpret_cast<f32x4*>(part + ((size_t)(kb * 2 + 1) * tp) * I + row) = u[m][0];
+    }
+}
+
+// h = bf16(silu(sum_kb gate) * (sum_kb up)), parts added in kb order, written as packed token
+// tiles for the down stream. One thread per 8 channels of one token slot (all 64 slots).
+__global__ __launch_bounds__(256) void dense_gu_finish_kernel(const float* __restrict__ part, int ks, int I,
+                                                              u16* __restrict__ hp) {
+    const int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int steps = I / 32;
+    if (o >= (int64_t)kDT * steps * 64) return;
+    const int l = (int)(o & 63);
+    const int64_t mj = o >> 6;
+    const int m = (int)(mj / steps), j = (int)(mj - (int64_t)m * steps);
+    const int t = 16 * m + (l & 15), n = 32 * j + 8 * (l >> 4);
+    const int tp = 16 * kDT;
+    float g[8], u[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) g[i] = u[i] = 0.0f;
+    for (int kb = 0; kb < ks; ++kb) {
+        const float* pg = part + ((size_t)kb * 2 * tp + t) * I + n;
+        const float* pu = part + ((size_t)(kb * 2 + 1) * tp + t) * I + n;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            g[i] += pg[i];
+            u[i] += pu[i];
+        }
+    }
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        w[i] = (uint32_t)f32_to_bf16(silu_mul(g[2 * i], u[2 * i])) |
+               ((uint32_t)f32_to_bf16(silu_mul(g[2 * i + 1], u[2 * i + 1])) << 16);
+    *reinterpret_cast<uint4*>(hp + o * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// part[kb][t][c] = partial sums of output channel c for token t over k-part kb of I.
+// grid: (d / 64, KS); block: 4 waves of 16 rows of Wd.
+template <bool PK>
+__global__ __launch_bounds__(256, 3) void dense_dn_stream_kernel(const u16* __restrict__ hp, const u16* __restrict__ Wd,
+                                                              float* __restrict__ part, int d, int I) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int n0 = (blockIdx.x * kWavesPerBlock + wave) * 16;
+    const int kb = blockIdx.y, kl = I / (int)gridDim.y, k0 = kb * kl;
+    const size_t wo = PK ? ((size_t)n0 / 16 * (I / 32) * 64 + lane) * 8 + (size_t)k0 * 16
+                         : (size_t)(n0 + (lane & 15)) * I + (lane >> 4) * 8 + k0;
+    const u16* const a[1] = {Wd + wo};
+    const u16* xb[kDT];
+#pragma unroll
+    for (int m = 0; m < kDT; ++m) xb[m] = hp + ((size_t)m * (I / 32) * 64 + lane) * 8 + (size_t)k0 * 16;
+    f32x4 acc[kDT][1];
+    zero_acc<kDT>(acc);
+    stream_core<1, kDT, kDDdn, kNT, PK, true>(a, xb, kl, acc);
+    const int tp = 16 * kDT;
+#pragma unroll
+    for (int m = 0; m < kDT; ++m)
+        *reinterpret_cast<f32x4*>(part + ((size_t)kb * tp + 16 * m + (lane & 15)) * d + n0 + 4 * (lane >> 4)) =
+            acc[m][0];
+}
+
+// y[t] = sum over kb, in order, of part[kb][t] for the T real tokens. One thread per float4.
+__global__ __launch_bounds__(256) void dense_dn_finish_kernel(const float* __restrict__ part, int ks, int64_t T, int d,
+                                                              float* __restrict__ y) {
+    const int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (o >= T * (d / 4)) return;
+    const int64_t t = o / (d / 4);
+    const int c = (int)(o - t * (d / 4)) * 4;
+    const int tp = 16 * kDT;
+    float4 acc = *reinterpret_cast<const float4*>(part + (size_t)t * d + c);
+    for (int kb = 1; kb < ks; ++kb) {
+        const float4 v = *reinterpret_cast<const float4*>(part + ((size_t)kb * tp + t) * d + c);
+        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    *reinterpret_cast<float4*>(y + t * d + c) = acc;
+}
+
+// k parts: the most (up to max_ks) that divide k into whole 32-wide steps.
+int dense_ks(int k, int max_ks) {
+    int ks = max_ks;
+    while (ks > 1 && k % (32 * ks) != 0) ks /= 2;
+    return ks;
+}
+
+constexpr int kDenseKsGU = 4, kDenseKsDN = 16;
 
 }  // namespace
 
@@ -367,7 +489,53 @@ void launch_combine(const Shape& s, const float* y_perm, const int32_t* pair_ran
 void launch_pack_stream(const void* W, void* P, int64_t rows, int K, hipStream_t st) {
     const int64_t chunks = (rows / 16) * (K / 32) * 64;            // rows * K / 8
     hipLaunchKernelGGL(pack_stream_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, st, (const u16*)W,
-                       (u16*)P, rows, K);
+                       (u16*)P, rows, rows, K);
+}
+
+bool dense_stream_supports(int64_t T, int d, int I) { return T >= 1 && T <= 16 * kDT && d % 64 == 0 && I % 64 == 0; }
+
+size_t dense_stream_workspace_bytes(int64_t T, int d, int I) {
+    (void)T;
+    const size_t tp = 16 * kDT;
+    auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+    return up(tp * d * 2) + up((size_t)dense_ks(d, kDenseKsGU) * 2 * tp * I * 4) + up(tp * I * 2) +
+           up((size_t)dense_ks(I, kDenseKsDN) * tp * d * 4);
+}
+
+void launch_dense_stream(int64_t T, int d, int I, bool packed, const void* x, const void* Wg, const void* Wu,
+                         const void* Wd, float* y, void* ws, hipStream_t st) {
+    const size_t tp = 16 * kDT;
+    auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+    const int ks_gu = dense_ks(d, kDenseKsGU), ks_dn = dense_ks(I, kDenseKsDN);
+    char* w = static_cast<char*>(ws);
+    u16* xp = reinterpret_cast<u16*>(w);
+    w += up(tp * d * 2);
+    float* part_gu = reinterpret_cast<float*>(w);
+    w += up((size_t)ks_gu * 2 * tp * I * 4);
+    u16* hp = reinterpret_cast<u16*>(w);
+    w += up(tp * I * 2);
+    float* part_dn = reinterpret_cast<float*>(w);
+    const int64_t xchunks = (int64_t)kDT * (d / 32) * 64;
+    hipLaunchKernelGGL(pack_stream_kernel, dim3((unsigned)((xchunks + 255) / 256)), dim3(256), 0, st, (const u16*)x,
+                       xp, (int64_t)tp, T, d);
+    if (packed)
+        hipLaunchKernelGGL(dense_gu_stream_kernel<true>, dim3((unsigned)(I / 64), (unsigned)ks_gu), dim3(256), 0, st,
+                           xp, (const u16*)Wg, (const u16*)Wu, part_gu, d, I);
+    else
+        hipLaunchKernelGGL(dense_gu_stream_kernel<false>, dim3((unsigned)(I / 64), (unsigned)ks_gu), dim3(256), 0, st,
+                           xp, (const u16*)Wg, (const u16*)Wu, part_gu, d, I);
+    const int64_t hchunks = (int64_t)kDT * (I / 32) * 64;
+    hipLaunchKernelGGL(dense_gu_finish_kernel, dim3((unsigned)((hchunks + 255) / 256)), dim3(256), 0, st, part_gu,
+                       ks_gu, I, hp);
+    if (packed)
+        hipLaunchKernelGGL(dense_dn_stream_kernel<true>, dim3((unsigned)(d / 64), (unsigned)ks_dn), dim3(256), 0, st,
+                           hp, (const u16*)Wd, part_dn, d, I);
+    else
+        hipLaunchKernelGGL(dense_dn_stream_kernel<false>, dim3((unsigned)(d / 64), (unsigned)ks_dn), dim3(256), 0, st,
+                           hp, (const u16*)Wd, part_dn, d, I);
+    const int64_t ychunks = T * (d / 4);
+    hipLaunchKernelGGL(dense_dn_finish_kernel, dim3((unsigned)((ychunks + 255) / 256)), dim3(256), 0, st, part_dn,
+                       ks_dn, T, d, y);
 }
 
 }  // namespace beam

@@ -363,21 +363,27 @@ void launch_gemm_down(const Shape& s, const void* h, const int32_t* offsets, con
 
 // Dense SwiGLU MLP (one expert, all T tokens in order): h = bf16(silu(x . Wg^T) * (x . Wu^T)),
 // then y = h . Wd^T in FP32.
-void launch_dense_swiglu(int64_t T, int d, int I, const void* x, const void* Wg, const void* Wu, void* h,
+void launch_dense_swiglu(int64_t T, int d, int I, bool packed, const void* x, const void* Wg, const void* Wu, void* h,
                          hipStream_t st) {
     const int n_nb = (I + GN / 2 - 1) / (GN / 2);
     const int items = (int)((T + GM - 1) / GM) * n_nb;
-    hipLaunchKernelGGL((grouped_gemm_kernel<0, true, false>), dim3((unsigned)((items + 7) / 8 * 8)), dim3(NT), 0, st,
-                       (const u16*)x, nullptr, nullptr, nullptr, nullptr, (const u16*)Wg, (const u16*)Wu, nullptr, 1,
-                       h, d, I, n_nb, (int)T);
+#define BEAM_DGU(PK)                                                                                          \
+    hipLaunchKernelGGL((grouped_gemm_kernel<0, true, PK>), dim3((unsigned)((items + 7) / 8 * 8)), dim3(NT), 0, st, \
+                       (const u16*)x, nullptr, nullptr, nullptr, nullptr, (const u16*)Wg, (const u16*)Wu, nullptr, 1, \
+                       h, d, I, n_nb, (int)T)
+    if (packed) BEAM_DGU(true); else BEAM_DGU(false);
+#undef BEAM_DGU
 }
 
-void launch_dense_down(int64_t T, int d, int I, const void* h, const void* Wd, float* y, hipStream_t st) {
+void launch_dense_down(int64_t T, int d, int I, bool packed, const void* h, const void* Wd, float* y, hipStream_t st) {
     const int n_nb = (d + GN - 1) / GN;
     const int items = (int)((T + GM - 1) / GM) * n_nb;
-    hipLaunchKernelGGL((grouped_gemm_kernel<1, true, false>), dim3((unsigned)((items + 7) / 8 * 8)), dim3(NT), 0, st,
-                       (const u16*)h, nullptr, nullptr, nullptr, nullptr, (const u16*)Wd, nullptr, nullptr, 1, y, I, d,
-                       n_nb, (int)T);
+#define BEAM_DDN(PK)                                                                                          \
+    hipLaunchKernelGGL((grouped_gemm_kernel<1, true, PK>), dim3((unsigned)((items + 7) / 8 * 8)), dim3(NT), 0, st, \
+                       (const u16*)h, nullptr, nullptr, nullptr, nullptr, (const u16*)Wd, nullptr, nullptr, 1, y, I, d, \
+                       n_nb, (int)T)
+    if (packed) BEAM_DDN(true); else BEAM_DDN(false);
+#undef BEAM_DDN
 }
 
 bool dense_supports(int64_t T, int d, int I) {

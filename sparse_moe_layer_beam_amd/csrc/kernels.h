@@ -65,9 +65,14 @@ void launch_down_fp8(const Shape& s, const void* h, const int32_t* offsets, cons
 
 // Dense SwiGLU MLP through the same GEMM (grouped_gemm.hip).
 bool dense_supports(int64_t T, int d, int I);
-void launch_dense_swiglu(int64_t T, int d, int I, const void* x, const void* Wg, const void* Wu, void* h,
+// Dense MLP for decode-sized batches (T <= 64): weight streams against packed token tiles.
+bool dense_stream_supports(int64_t T, int d, int I);
+size_t dense_stream_workspace_bytes(int64_t T, int d, int I);
+void launch_dense_stream(int64_t T, int d, int I, bool packed, const void* x, const void* Wg, const void* Wu,
+                         const void* Wd, float* y, void* ws, hipStream_t st);
+void launch_dense_swiglu(int64_t T, int d, int I, bool packed, const void* x, const void* Wg, const void* Wu, void* h,
                          hipStream_t st);
-void launch_dense_down(int64_t T, int d, int I, const void* h, const void* Wd, float* y, hipStream_t st);
+void launch_dense_down(int64_t T, int d, int I, bool packed, const void* h, const void* Wd, float* y, hipStream_t st);
 
 // Post-MLP RMSNorm + depth-scaled residual (residual.hip); rows of up to kPostMaxD floats.
 constexpr int kPostMaxD = 16384;

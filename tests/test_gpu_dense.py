@@ -1,6 +1,8 @@
 """Dense SwiGLU MLP on the GPU (beam_moe_dense_mlp, through the C ABI) against the oracle's
-expert() in double: every token at mid size and at ragged token counts, sampled tokens at
-the Beam dense shape (d=5120, I=20480), bitwise run-to-run determinism."""
+expert() in double: every token at mid size and at ragged token counts (T <= 64 takes the
+weight-streaming path, larger T the tiled GEMM), sampled tokens at the Beam dense shape
+(d=5120, I=20480), bitwise run-to-run determinism, and packed weights bitwise equal to
+row-major ones."""
 import numpy as np
 import pytest
 
@@ -17,10 +19,13 @@ pytestmark = pytest.mark.gpu
 MID = recipes.DENSE_WORKLOADS[12]
 
 
-def _run(w, t):
+def _run(w, t, packed=None):
     ws = torch.empty(max(1, moe.beam_moe_dense_workspace_bytes(w.T, w.d, w.I)), dtype=torch.uint8, device="cuda")
     y = torch.full((w.T, w.d), float("nan"), dtype=torch.float32, device="cuda")
-    moe.beam_moe_dense_mlp(w.T, w.d, w.I, t["x"], t["Wg"], t["Wu"], t["Wd"], y, ws)
+    if packed is None:
+        moe.beam_moe_dense_mlp(w.T, w.d, w.I, t["x"], t["Wg"], t["Wu"], t["Wd"], y, ws)
+    else:
+        moe.beam_moe_dense_mlp(w.T, w.d, w.I, t["x"], *packed, y, ws, weight_layout=moe.WEIGHTS_PACKED)
     torch.cuda.synchronize()
     return y.cpu().numpy()
 
@@ -43,6 +48,8 @@ def test_dense_mid_every_token(T):
     print("dense mid T=%d: max|dy| %.3e, rms %.3e" % (T, err, rms))
     assert np.isfinite(y).all()
     assert err <= P.Y_TOL * rms
+    yp = _run(w, t, moe.pack_dense_weights(t["Wg"], t["Wu"], t["Wd"]))
+    assert np.array_equal(y.view(np.uint32), yp.view(np.uint32))
 
 
 @pytest.mark.parametrize("cfg", [10, 11])
@@ -53,6 +60,8 @@ def test_dense_beam_shape_sampled(cfg):
     y = _run(w, t)
     y2 = _run(w, t)
     assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+    y3 = _run(w, t, moe.pack_dense_weights(t["Wg"], t["Wu"], t["Wd"]))
+    assert np.array_equal(y.view(np.uint32), y3.view(np.uint32))
     rng = np.random.default_rng(cfg)
     rows = sorted({0, w.T - 1, *rng.choice(w.T, size=min(6, w.T), replace=False).tolist()})
     wg, wu, wd = synth.dense_weights(w)
