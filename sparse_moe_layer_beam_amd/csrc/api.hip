@@ -37,6 +37,7 @@ beam_moe_status to_shape(const beam_moe_shape* p, Shape* s) {
     s->T = p->T; s->d = p->d; s->E = p->E; s->G = p->n_group; s->KG = p->topk_group; s->K = p->top_k; s->I = p->I;
     s->S = p->routed_scaling_factor; s->norm = p->norm_topk_prob ? 1 : 0; s->eps = p->rms_eps;
     s->packed = p->weight_layout == BEAM_MOE_WEIGHTS_PACKED ? 1 : 0;
+    s->route_E = p->E;
     return BEAM_MOE_OK;
 }
 
@@ -359,8 +360,8 @@ beam_moe_status beam_moe_experts_share(const beam_moe_shape* shape, int32_t e_be
         !aligned(y_part))
         return BEAM_MOE_ERR_INVALID_ARG;
     if (s.T == 0) return BEAM_MOE_OK;
-    Shape sl = s;                 // the local experts are the whole expert set of this call
-    sl.E = e_count;
+    Shape sl = s;                 // the local experts are the whole expert set of this call;
+    sl.E = e_count;               // the path (streams or tiled GEMM) is still chosen on all E
     const Layout L = layout(sl);
     if (!workspace || !aligned(workspace)) return BEAM_MOE_ERR_INVALID_ARG;
     if (ws_bytes < L.total) return BEAM_MOE_ERR_WORKSPACE_TOO_SMALL;

@@ -27,29 +27,28 @@ namespace {
 #define BEAM_GU_DEPTH 6         // gate/up: k-steps of 32 prefetched ahead of the MFMAs
 #endif
 #ifndef BEAM_DN_DEPTH
-#define BEAM_DN_DEPTH 6         // down: the same
+#define BEAM_DN_DEPTH 8         // down: the same
+#endif
+#ifndef BEAM_GU_OCC
+#define BEAM_GU_OCC 3           // gate/up: blocks of 4 waves per CU the registers must allow
+#endif
+#ifndef BEAM_DN_OCC
+#define BEAM_DN_OCC 3           // down: the same
 #endif
 #ifndef BEAM_STREAM_MT
 #define BEAM_STREAM_MT 1        // 16-token tiles per pass over an expert's weights
 #endif
-#ifndef BEAM_STREAM_PIN
-#define BEAM_STREAM_PIN 0       // 1: forbid scheduling across ring steps
-#endif
-#ifndef BEAM_STREAM_NT
-#define BEAM_STREAM_NT 0        // 1: non-temporal weight loads
-#endif
 #ifndef BEAM_GU_KSPLIT
-#define BEAM_GU_KSPLIT 1        // gate/up: waves sharing one 16-channel group, each a part of k
+#define BEAM_GU_KSPLIT 4        // gate/up: waves sharing one 16-channel group, each a part of k
 #endif
 #ifndef BEAM_DN_KSPLIT
-#define BEAM_DN_KSPLIT 2        // down: the same (2 measured 2% faster; gate/up measured slower split)
+#define BEAM_DN_KSPLIT 2        // down: the same
 #endif
 
 constexpr int kWavesPerBlock = 4;
 constexpr int kDgu = BEAM_GU_DEPTH;
 constexpr int kDdn = BEAM_DN_DEPTH;
 constexpr int kMT = BEAM_STREAM_MT;
-constexpr bool kNT = BEAM_STREAM_NT != 0;
 // Weight elements per unit of k: 1 row-major, 16 packed (a 32-k step of a 16-row block is 512
 // contiguous elements).
 template <bool PK>
@@ -57,11 +56,6 @@ constexpr int kWStep = PK ? 16 : 1;
 
 __device__ __forceinline__ bf16x8 ld8(const u16* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
-template <bool NT>
-__device__ __forceinline__ bf16x8 ldw(const u16* p) {
-    if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(p));
-    else return ld8(p);
-}
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -73,7 +67,7 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 // D*(RB+MT) 16-byte loads in flight without register copies. Prefetch addresses past the end
 // are clamped to the last step (a redundant, in-bounds load that is never consumed); the
 // (K/32) % D leftover steps are taken from the ring after the main loop.
-template <int RB, int MT, int D, bool NT, bool PK, bool PT = false>
+template <int RB, int MT, int D, bool PK, bool PT = false>
 __device__ __forceinline__ void stream_core(const u16* const (&a)[RB], const u16* const (&b)[MT], int K,
                                             f32x4 (&acc)[MT][RB]) {
     bf16x8 wa[D][RB], xb[D][MT];
@@ -84,10 +78,9 @@ __device__ __forceinline__ void stream_core(const u16* const (&a)[RB], const u16
     for (int s = 0; s < D; ++s) {
         const int k = min(s * 32, last);
 #pragma unroll
-        for (int r = 0; r < RB; ++r) wa[s][r] = ldw<NT>(a[r] + k * kWStep<PK>);
+        for (int r = 0; r < RB; ++r) wa[s][r] = ld8(a[r] + k * kWStep<PK>);
 #pragma unroll
         for (int m = 0; m < MT; ++m) xb[s][m] = ld8(b[m] + k * kWStep<PT>);
-        if constexpr (BEAM_STREAM_PIN != 0) __builtin_amdgcn_sched_barrier(0);
     }
     for (int k0 = 0; k0 < kfull; k0 += 32 * D) {
 #pragma unroll
@@ -98,10 +91,9 @@ __device__ __forceinline__ void stream_core(const u16* const (&a)[RB], const u16
                 for (int r = 0; r < RB; ++r) acc[m][r] = mfma16(wa[s][r], xb[s][m], acc[m][r]);
             const int kn = min(k0 + (s + D) * 32, last);
 #pragma unroll
-            for (int r = 0; r < RB; ++r) wa[s][r] = ldw<NT>(a[r] + kn * kWStep<PK>);
+            for (int r = 0; r < RB; ++r) wa[s][r] = ld8(a[r] + kn * kWStep<PK>);
 #pragma unroll
             for (int m = 0; m < MT; ++m) xb[s][m] = ld8(b[m] + kn * kWStep<PT>);
-            if constexpr (BEAM_STREAM_PIN != 0) __builtin_amdgcn_sched_barrier(0);
         }
     }
     const int rem = nsteps - kfull / 32;
@@ -154,10 +146,12 @@ __device__ __forceinline__ void ksplit_reduce(f32x4 (&part)[kWavesPerBlock][NA][
 // in LDS. A wave streams one 16-row block at a time, which keeps the number of DRAM rows
 // open across the chip low, which is what sets the achieved bandwidth here. Splitting k
 // shortens each block, and with it the tail of the launch, where fewer and fewer blocks
-// are left to keep the memory busy. Three waves per SIMD with a 6-deep ring measured
-// faster than two with 8 (same bytes in flight, more streams to hide the stalls of each).
+// are left to keep the memory busy. Measured on MI355X with packed weights: k in 4 parts
+// and a 6-deep ring at three waves per SIMD here, an 8-deep ring at three waves per SIMD
+// for down, 1.5% faster than one part and depth 6 at four waves; an 8-deep gate/up ring
+// at three waves per SIMD ran 6% slower.
 template <int KS, bool PK>
-__global__ __launch_bounds__(256, 3) void swiglu_stream_kernel(const u16* __restrict__ x,
+__global__ __launch_bounds__(256, BEAM_GU_OCC) void swiglu_stream_kernel(const u16* __restrict__ x,
                                                             const int32_t* __restrict__ offsets,
                                                             const int32_t* __restrict__ sorted_pairs, int K,
                                                             const u16* __restrict__ Wg, const u16* __restrict__ Wu,
@@ -191,8 +185,8 @@ __global__ __launch_bounds__(256, 3) void swiglu_stream_kernel(const u16* __rest
         f32x4 gu[2][kMT][1];
         zero_acc<kMT>(gu[0]);
         zero_acc<kMT>(gu[1]);
-        stream_core<1, kMT, kDgu, kNT, PK>(ag, xp, kl, gu[0]);
-        stream_core<1, kMT, kDgu, kNT, PK>(au, xp, kl, gu[1]);
+        stream_core<1, kMT, kDgu, PK>(ag, xp, kl, gu[0]);
+        stream_core<1, kMT, kDgu, PK>(au, xp, kl, gu[1]);
         ksplit_reduce<KS, kMT, 2>(part, wave, lane, gu);
         // lane holds channels n0 + 4*(lane/16) + i for token row mb + 16*mt + lane%16
         if (writer)
@@ -216,7 +210,7 @@ __global__ __launch_bounds__(256, 3) void swiglu_stream_kernel(const u16* __rest
 // grid: (ceil(d / (16 * 4 / KS)), E); block: 4 waves; the KS waves of a 16-row group of Wd
 // each stream a 1/KS part of k, as in the gate/up kernel.
 template <int KS, bool PK>
-__global__ __launch_bounds__(256) void down_stream_kernel(const u16* __restrict__ h,
+__global__ __launch_bounds__(256, BEAM_DN_OCC) void down_stream_kernel(const u16* __restrict__ h,
                                                           const int32_t* __restrict__ offsets,
                                                           const int32_t* __restrict__ sorted_pairs,
                                                           const float* __restrict__ topk_w,
@@ -245,7 +239,7 @@ __global__ __launch_bounds__(256) void down_stream_kernel(const u16* __restrict_
         for (int mt = 0; mt < kMT; ++mt) hp[mt] = h + (size_t)(beg + min(mb + 16 * mt + r16, n_e - 1)) * I + kq;
         f32x4 acc[1][kMT][1];
         zero_acc<kMT>(acc[0]);
-        stream_core<1, kMT, kDdn, kNT, PK>(a, hp, kl, acc[0]);
+        stream_core<1, kMT, kDdn, PK>(a, hp, kl, acc[0]);
         ksplit_reduce<KS, kMT, 1>(part, wave, lane, acc);
         if (writer)
 #pragma unroll
@@ -336,8 +330,8 @@ __global__ __launch_bounds__(256, 3) void dense_gu_stream_kernel(const u16* __re
     f32x4 g[kDT][1], u[kDT][1];
     zero_acc<kDT>(g);
     zero_acc<kDT>(u);
-    stream_core<1, kDT, kDDgu, kNT, PK, true>(ag, xb, kl, g);
-    stream_core<1, kDT, kDDgu, kNT, PK, true>(au, xb, kl, u);
+    stream_core<1, kDT, kDDgu, PK, true>(ag, xb, kl, g);
+    stream_core<1, kDT, kDDgu, PK, true>(au, xb, kl, u);
     // lane holds channels n0 + 4 (lane / 16) + i for token 16 m + lane % 16
     const int tp = 16 * kDT;
 #pragma unroll
@@ -396,7 +390,7 @@ __global__ __launch_bounds__(256, 3) void dense_dn_stream_kernel(const u16* __re
     for (int m = 0; m < kDT; ++m) xb[m] = hp + ((size_t)m * (I / 32) * 64 + lane) * 8 + (size_t)k0 * 16;
     f32x4 acc[kDT][1];
     zero_acc<kDT>(acc);
-    stream_core<1, kDT, kDDdn, kNT, PK, true>(a, xb, kl, acc);
+    stream_core<1, kDT, kDDdn, PK, true>(a, xb, kl, acc);
     const int tp = 16 * kDT;
 #pragma unroll
     for (int m = 0; m < kDT; ++m)
@@ -434,7 +428,9 @@ constexpr int kDenseKsGU = 4, kDenseKsDN = 16;
 // Path choice from the average number of tokens per expert: up to 16 the weight-streaming
 // kernels (each expert's weights read once per 16 of its tokens), above that the tiled
 // grouped GEMM (weights read about once per call, tokens re-read from L2).
-bool experts_tiled(const Shape& s) { return gemm_supports(s) && s.T * (int64_t)s.K > 16 * (int64_t)s.E; }
+// An expert-parallel share decides on all experts (route_E), so that it takes the same path,
+// with the same arithmetic, as the whole layer would.
+bool experts_tiled(const Shape& s) { return gemm_supports(s) && s.T * (int64_t)s.K > 16 * (int64_t)s.route_E; }
 
 int experts_tile_m(const Shape& s) { return experts_tiled(s) ? gemm_tile_m() : 16 * kMT; }
 

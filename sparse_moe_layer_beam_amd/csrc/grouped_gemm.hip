@@ -287,11 +287,7 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(
     // This wave's part of the tile: tokens 128*(wave % 2) .. +128, and four 16-row weight
     // subtiles (gate/up: 32 gate rows and the matching 32 up rows; down: 64 rows), as rows
     // of a weight buffer.
-#if BEAM_GEMM_WSWAP
-    const int wm = wave >> 2, wn = wave & 3;
-#else
     const int wm = wave & 1, wn = wave >> 1;
-#endif
     const int tok0 = 128 * wm;
     int wrow[4], c0;
     if constexpr (MODE == 0) {
@@ -388,7 +384,7 @@ void launch_dense_down(int64_t T, int d, int I, bool packed, const void* h, cons
 
 bool dense_supports(int64_t T, int d, int I) {
     Shape s{};
-    s.T = T; s.d = d; s.I = I; s.K = 1; s.E = 1;
+    s.T = T; s.d = d; s.I = I; s.K = 1; s.E = 1; s.route_E = 1;
     return gemm_supports(s);
 }
 

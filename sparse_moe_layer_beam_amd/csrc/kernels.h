@@ -13,6 +13,7 @@ struct Shape {
     int norm;
     float eps;
     int packed;     // expert weights in the packed layout of beam_moe_pack_weights
+    int route_E;    // experts the routing spreads the pairs over (E, or all experts for a share)
 };
 
 // Router (router.hip)
