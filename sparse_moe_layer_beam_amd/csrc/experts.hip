@@ -17,6 +17,10 @@
 // wave loads (lane l: row l % 16, k 8(l / 16) .. +8). Row-major, one load instruction reads
 // 64 bytes from each of 16 rows; packed, it reads 1 KB that is contiguous, and the stream
 // runs at 6.2-6.3 TB/s instead of 5.6 on MI355X (same values, bitwise-equal results).
+//
+// Also here: the packing kernel itself, and the dense SwiGLU MLP for decode-sized batches
+// (Transformers "Beam" page, Overview: the first 3 layers use a dense MLP), which streams its
+// weights the same way against packed 16-token tiles.
 #include "common.h"
 #include "kernels.h"
 
@@ -55,7 +59,6 @@ template <bool PK>
 constexpr int kWStep = PK ? 16 : 1;
 
 __device__ __forceinline__ bf16x8 ld8(const u16* p) { return *reinterpret_cast<const bf16x8*>(p); }
-
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);

@@ -26,6 +26,9 @@
 //    so that LDS row r holds global 16-byte chunk c at position c ^ (r % 8). The MFMA
 //    fragment reads (16 rows x one chunk) then hit eight different positions per eight
 //    lanes and stay free of bank conflicts without padding.
+//  * Weights in the packed layout (beam_moe_pack_weights) arrive in MFMA fragment order:
+//    each direct load copies one contiguous kilobyte (a 16-row block's 32-k step) and the
+//    fragment reads index it directly, no swizzle. Same results, same speed here.
 #include "common.h"
 #include "kernels.h"
 
