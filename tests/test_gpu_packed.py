@@ -89,7 +89,7 @@ def test_pack_beam_expert_slab():
 
 
 @pytest.mark.parametrize("name", ["tiny", "mid_T77", "mid_T2000", "mid_prenorm_T333", "e128_T300", "e64_T150",
-                                  "e1024_T200"])
+                                  "e1024_T200", "mid_conc_T64", "mid_conc_T2000"])
 def test_forward_packed_bitwise_small(name):
     w = SMALL[name]
     print("case packed", name, flush=True)
@@ -113,9 +113,10 @@ def test_forward_packed_against_oracle_mid():
     assert err <= P.Y_TOL * rms
 
 
-@pytest.mark.parametrize("cfg", [1, 2])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
 def test_forward_packed_bitwise_beam(cfg):
-    """Beam decode (weight streams) and prefill (grouped GEMM): packed equals row-major bit for bit."""
+    """Every Beam workload (decode streams; prefill, skewed and large-chunk grouped GEMMs): packed
+    equals row-major bit for bit."""
     w = recipes.WORKLOADS[cfg]
     print("case packed beam", w.name, flush=True)
     t = synth.device_inputs(w)

@@ -30,6 +30,10 @@ SMALL = {
     "e1024_T200": Workload(26, "e1024_T200", T=200, d=256, E=1024, n_group=16, topk_group=4, top_k=16, I=64),
     "e64_T150": Workload(27, "e64_T150", T=150, d=128, E=64, n_group=8, topk_group=3, top_k=5, I=64),
     "mid_nonorm_T100": Workload(28, "mid_nonorm_T100", T=100, norm_topk_prob=False, **_MID),
+    # concentrated routing: 8 experts with a +5 bias take most pairs, so single experts see every
+    # token (the weight streams' multi-tile loop; the GEMM's many m-tiles of one expert)
+    "mid_conc_T64": Workload(29, "mid_conc_T64", T=64, hot_experts=8, hot_bias=5.0, **_MID),
+    "mid_conc_T2000": Workload(30, "mid_conc_T2000", T=2000, hot_experts=8, hot_bias=5.0, **_MID),
 }
 BEAM = {i: recipes.WORKLOADS[i] for i in (1, 2, 3, 4)}
 
