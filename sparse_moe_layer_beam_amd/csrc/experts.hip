@@ -312,7 +312,7 @@ __global__ __launch_bounds__(256) void pack_stream_kernel(const u16* __restrict_
 // 16 weight rows over a 1/KS part of k against the four tiles, and the KS parts meet in a
 // fixed-order reduction that also applies the SwiGLU (gate/up) or writes y (down).
 constexpr int kDT = 4;                   // token tiles (64 tokens)
-constexpr int kDDgu = 3, kDDdn = 4;      // ring depths of the dense streams (gate/up holds both accumulators)
+constexpr int kDDgu = 3, kDDdn = 3;      // ring depths of the dense streams
 
 // part[kb][0|1][t][n] = partial gate|up sums of channel n for token t over k-part kb.
 // grid: (I / 64, KS); block: 4 waves of 16 channels.
@@ -325,23 +325,22 @@ __global__ __launch_bounds__(256, 3) void dense_gu_stream_kernel(const u16* __re
     const int kb = blockIdx.y, kl = d / (int)gridDim.y, k0 = kb * kl;
     const size_t wo = PK ? ((size_t)n0 / 16 * (d / 32) * 64 + lane) * 8 + (size_t)k0 * 16
                          : (size_t)(n0 + (lane & 15)) * d + (lane >> 4) * 8 + k0;
-    const u16* const ag[1] = {Wg + wo};
-    const u16* const au[1] = {Wu + wo};
+    // gate and up rows of the same channels in one pass: each token fragment feeds both
+    const u16* const a[2] = {Wg + wo, Wu + wo};
     const u16* xb[kDT];
 #pragma unroll
     for (int m = 0; m < kDT; ++m) xb[m] = xp + ((size_t)m * (d / 32) * 64 + lane) * 8 + (size_t)k0 * 16;
-    f32x4 g[kDT][1], u[kDT][1];
-    zero_acc<kDT>(g);
-    zero_acc<kDT>(u);
-    stream_core<1, kDT, kDDgu, PK, true>(ag, xb, kl, g);
-    stream_core<1, kDT, kDDgu, PK, true>(au, xb, kl, u);
+    f32x4 acc[kDT][2];
+#pragma unroll
+    for (int m = 0; m < kDT; ++m) acc[m][0] = acc[m][1] = f32x4{0, 0, 0, 0};
+    stream_core<2, kDT, kDDgu, PK, true>(a, xb, kl, acc);
     // lane holds channels n0 + 4 (lane / 16) + i for token 16 m + lane % 16
     const int tp = 16 * kDT;
 #pragma unroll
     for (int m = 0; m < kDT; ++m) {
         const size_t row = (size_t)(16 * m + (lane & 15)) * I + n0 + 4 * (lane >> 4);
-        *reinterpret_cast<f32x4*>(part + ((size_t)kb * 2 * tp) * I + row) = g[m][0];
-        *reinterpret_cast<f32x4*>(part + ((size_t)(kb * 2 + 1) * tp) * I + row) = u[m][0];
+        *reinterpret_cast<f32x4*>(part + ((size_t)kb * 2 * tp) * I + row) = acc[m][0];
+        *reinterpret_cast<f32x4*>(part + ((size_t)(kb * 2 + 1) * tp) * I + row) = acc[m][1];
     }
 }
 
@@ -383,22 +382,29 @@ template <bool PK>
 __global__ __launch_bounds__(256, 3) void dense_dn_stream_kernel(const u16* __restrict__ hp, const u16* __restrict__ Wd,
                                                               float* __restrict__ part, int d, int I) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int n0 = (blockIdx.x * kWavesPerBlock + wave) * 16;
+    const int n0 = (blockIdx.x * kWavesPerBlock + wave) * 32;          // two 16-row blocks of Wd
     const int kb = blockIdx.y, kl = I / (int)gridDim.y, k0 = kb * kl;
-    const size_t wo = PK ? ((size_t)n0 / 16 * (I / 32) * 64 + lane) * 8 + (size_t)k0 * 16
-                         : (size_t)(n0 + (lane & 15)) * I + (lane >> 4) * 8 + k0;
-    const u16* const a[1] = {Wd + wo};
+    const u16* a[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int nr = n0 + 16 * r;
+        a[r] = Wd + (PK ? ((size_t)nr / 16 * (I / 32) * 64 + lane) * 8 + (size_t)k0 * 16
+                        : (size_t)(nr + (lane & 15)) * I + (lane >> 4) * 8 + k0);
+    }
     const u16* xb[kDT];
 #pragma unroll
     for (int m = 0; m < kDT; ++m) xb[m] = hp + ((size_t)m * (I / 32) * 64 + lane) * 8 + (size_t)k0 * 16;
-    f32x4 acc[kDT][1];
-    zero_acc<kDT>(acc);
-    stream_core<1, kDT, kDDdn, PK, true>(a, xb, kl, acc);
+    f32x4 acc[kDT][2];
+#pragma unroll
+    for (int m = 0; m < kDT; ++m) acc[m][0] = acc[m][1] = f32x4{0, 0, 0, 0};
+    stream_core<2, kDT, kDDdn, PK, true>(a, xb, kl, acc);
     const int tp = 16 * kDT;
 #pragma unroll
     for (int m = 0; m < kDT; ++m)
-        *reinterpret_cast<f32x4*>(part + ((size_t)kb * tp + 16 * m + (lane & 15)) * d + n0 + 4 * (lane >> 4)) =
-            acc[m][0];
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+            *reinterpret_cast<f32x4*>(part + ((size_t)kb * tp + 16 * m + (lane & 15)) * d + n0 + 16 * r +
+                                      4 * (lane >> 4)) = acc[m][r];
 }
 
 // y[t] = sum over kb, in order, of part[kb][t] for the T real tokens. One thread per float4.
@@ -424,7 +430,7 @@ int dense_ks(int k, int max_ks) {
     return ks;
 }
 
-constexpr int kDenseKsGU = 4, kDenseKsDN = 16;
+constexpr int kDenseKsGU = 4, kDenseKsDN = 32;
 
 }  // namespace
 
@@ -491,7 +497,7 @@ void launch_pack_stream(const void* W, void* P, int64_t rows, int K, hipStream_t
                        (u16*)P, rows, rows, K);
 }
 
-bool dense_stream_supports(int64_t T, int d, int I) { return T >= 1 && T <= 16 * kDT && d % 64 == 0 && I % 64 == 0; }
+bool dense_stream_supports(int64_t T, int d, int I) { return T >= 1 && T <= 16 * kDT && d % 128 == 0 && I % 64 == 0; }
 
 size_t dense_stream_workspace_bytes(int64_t T, int d, int I) {
     (void)T;
@@ -527,10 +533,10 @@ void launch_dense_stream(int64_t T, int d, int I, bool packed, const void* x, co
     hipLaunchKernelGGL(dense_gu_finish_kernel, dim3((unsigned)((hchunks + 255) / 256)), dim3(256), 0, st, part_gu,
                        ks_gu, I, hp);
     if (packed)
-        hipLaunchKernelGGL(dense_dn_stream_kernel<true>, dim3((unsigned)(d / 64), (unsigned)ks_dn), dim3(256), 0, st,
+        hipLaunchKernelGGL(dense_dn_stream_kernel<true>, dim3((unsigned)(d / 128), (unsigned)ks_dn), dim3(256), 0, st,
                            hp, (const u16*)Wd, part_dn, d, I);
     else
-        hipLaunchKernelGGL(dense_dn_stream_kernel<false>, dim3((unsigned)(d / 64), (unsigned)ks_dn), dim3(256), 0, st,
+        hipLaunchKernelGGL(dense_dn_stream_kernel<false>, dim3((unsigned)(d / 128), (unsigned)ks_dn), dim3(256), 0, st,
                            hp, (const u16*)Wd, part_dn, d, I);
     const int64_t ychunks = T * (d / 4);
     hipLaunchKernelGGL(dense_dn_finish_kernel, dim3((unsigned)((ychunks + 255) / 256)), dim3(256), 0, st, part_dn,
