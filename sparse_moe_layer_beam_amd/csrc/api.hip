@@ -322,6 +322,8 @@ beam_moe_status beam_moe_dense_mlp(int64_t T, int32_t d, int32_t I, int32_t weig
         return BEAM_MOE_ERR_INVALID_ARG;
     if (!x || !Wg || !Wu || !Wd || !y) return BEAM_MOE_ERR_INVALID_ARG;
     if (!aligned(x) || !aligned(Wg) || !aligned(Wu) || !aligned(Wd) || !aligned(y)) return BEAM_MOE_ERR_INVALID_ARG;
+    const int64_t lim = (int64_t)1 << 31;
+    if (T * (int64_t)d >= lim || T * (int64_t)I >= lim || (int64_t)d * I >= lim) return BEAM_MOE_ERR_UNSUPPORTED_SHAPE;
     const bool stream_path = beam::dense_stream_supports(T, d, I);
     if (!stream_path && !beam::dense_supports(T, d, I)) return BEAM_MOE_ERR_UNSUPPORTED_SHAPE;
     if (T == 0) return BEAM_MOE_OK;

@@ -184,6 +184,7 @@ def test_dense_mlp_validates_before_launching():
     assert moe.beam_moe_dense_mlp(64, 5120, 20480, A, A, A, A, A, WS(n), weight_layout=2, stream=0,
                                   check=False) == INVALID
     assert f(-3, 5120, 20480, A, A, A, A, A, WS(n)) == INVALID
+    assert f(1 << 20, 5120, 20480, A, A, A, A, A, WS(n)) == UNSUPPORTED   # T * I reaches 2^31
     assert f(0, 5120, 20480, A, A, A, A, A, None) == OK
 
 
