@@ -26,7 +26,9 @@
  *     failed launch and may follow earlier launches of the same call).
  *   - T = 0 returns BEAM_MOE_OK with no launch.
  *   - Weight layouts follow the (out_features, in_features) convention of linear
- *     layers: Wg, Wu [E, I, d]; Wd [E, d, I]; the router weight is Wr [d, E] FP32.
+ *     layers: Wg, Wu [E, I, d]; Wd [E, d, I]; the router weight is Wr [d, E] FP32. The
+ *     expert weights may instead be given in the packed layout of beam_moe_pack_weights,
+ *     as beam_moe_shape.weight_layout says (same values, same results, faster streams).
  *
  * Supported shapes (else BEAM_MOE_ERR_UNSUPPORTED_SHAPE): d and I multiples of 64;
  * E <= 64, or E in {128, 256, 512, 1024}; E % n_group == 0; n_group <= 64; the
