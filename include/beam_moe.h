@@ -260,8 +260,9 @@ beam_moe_status beam_moe_experts_share(const beam_moe_shape* shape, int32_t e_be
  * Pointers 16-byte aligned; rows * K below 2^40. rows = 0 returns BEAM_MOE_OK. */
 beam_moe_status beam_moe_pack_weights(int64_t rows, int32_t K, const void* w, void* packed, void* stream);
 
-/* Static, human-readable name of a status code. */
-const char* beam_moe_status_string(beam_moe_status status);
+/* Static, human-readable name of a status code; "unknown status" for any other value (the
+ * argument is a plain int so that any value a caller passes is well defined). */
+const char* beam_moe_status_string(int32_t status);
 
 #ifdef __cplusplus
 }

@@ -13,14 +13,16 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB = os.path.join(_HERE, "libbeam_oracle.so")
+_BUILT = os.path.join(_HERE, "libbeam_oracle.so")
+# BEAM_ORACLE_LIB: load another build of the same source instead (a sanitizer build, for instance)
+LIB = os.environ.get("BEAM_ORACLE_LIB") or _BUILT
 
 _c_i32p = ctypes.POINTER(ctypes.c_int32)
 
 
 def build() -> None:
     cmd = ["g++", "-O3", "-std=c++17", "-ffp-contract=off", "-fPIC", "-shared", "-pthread",
-           os.path.join(_HERE, "beam_oracle.cpp"), "-o", LIB]
+           os.path.join(_HERE, "beam_oracle.cpp"), "-o", _BUILT]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("oracle build failed:\n" + r.stderr)

@@ -11,7 +11,8 @@ import ctypes
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libbeam_moe.so")
+# BEAM_MOE_LIB: load another build of the same sources instead (a host-sanitizer build, for instance)
+LIB_PATH = os.environ.get("BEAM_MOE_LIB") or os.path.join(_PKG, "libbeam_moe.so")
 
 BEAM_MOE_OK = 0
 BEAM_MOE_ERR_INVALID_ARG = 1

@@ -405,7 +405,7 @@ beam_moe_status beam_moe_pack_weights(int64_t rows, int32_t K, const void* w, vo
     return hip_status();
 }
 
-const char* beam_moe_status_string(beam_moe_status status) {
+const char* beam_moe_status_string(int32_t status) {
     switch (status) {
         case BEAM_MOE_OK: return "ok";
         case BEAM_MOE_ERR_INVALID_ARG: return "invalid argument";

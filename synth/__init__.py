@@ -16,7 +16,9 @@ from .recipes import (WORKLOADS, Workload, DENSE_WORKLOADS, DenseWorkload, TID_X
                       TID_H, TID_NORMW, TID_HOT, TID_RESID, TID_POSTW)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-HOST_LIB = os.path.join(_HERE, "libsynth_host.so")
+_HOST_BUILT = os.path.join(_HERE, "libsynth_host.so")
+# BEAM_SYNTH_HOST_LIB: load another build of synth_host.c instead (a sanitizer build, for instance)
+HOST_LIB = os.environ.get("BEAM_SYNTH_HOST_LIB") or _HOST_BUILT
 DEV_LIB = os.path.join(_HERE, "libsynth_dev.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -27,7 +29,7 @@ def build(verbose: bool = False) -> None:
     """Compile the host generator (gcc) and the device generator (hipcc, gfx950)."""
     cmds = [
         ["gcc", "-O2", "-ffp-contract=off", "-fPIC", "-shared", "-pthread",
-         os.path.join(_HERE, "synth_host.c"), "-o", HOST_LIB, "-lm"],
+         os.path.join(_HERE, "synth_host.c"), "-o", _HOST_BUILT, "-lm"],
         [HIPCC, "--offload-arch=gfx950", "-O3", "-ffp-contract=off", "-fPIC", "-shared",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          os.path.join(_HERE, "synth_dev.hip"), "-o", DEV_LIB],
