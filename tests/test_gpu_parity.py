@@ -34,6 +34,14 @@ SMALL = {
     # token (the weight streams' multi-tile loop; the GEMM's many m-tiles of one expert)
     "mid_conc_T64": Workload(29, "mid_conc_T64", T=64, hot_experts=8, hot_bias=5.0, **_MID),
     "mid_conc_T2000": Workload(30, "mid_conc_T2000", T=2000, hot_experts=8, hot_bias=5.0, **_MID),
+    # degenerate routing shapes: every group kept (plain top-k), one expert per token, no groups
+    "e64_allgroups_T100": Workload(31, "e64_allgroups_T100", T=100, d=128, E=64, n_group=8, topk_group=8, top_k=6,
+                                   I=64),
+    "k1_T100": Workload(32, "k1_T100", T=100, d=256, E=32, n_group=4, topk_group=2, top_k=1, I=128),
+    "g1_T100": Workload(33, "g1_T100", T=100, d=256, E=256, n_group=1, topk_group=1, top_k=8, I=128),
+    # d not a multiple of 128: many tokens per expert but no tiled GEMM, so the weight streams
+    # run 16-token tile after tile
+    "d192_T500": Workload(34, "d192_T500", T=500, d=192, E=16, n_group=4, topk_group=2, top_k=4, I=192),
 }
 BEAM = {i: recipes.WORKLOADS[i] for i in (1, 2, 3, 4)}
 
