@@ -68,7 +68,7 @@ Layout layout(const Shape& s) {
     L.sp = o; o += up(P * 4);
     L.pr = o; o += up(P * 4);
     L.tiles = o; o += up(max_tiles * 4 * 4);
-    L.ntiles = o; o += up(4);
+    L.ntiles = o; o += up(beam::kTileWords * 4);
     L.h = o; o += up(P * s.I * 2);
     L.yp = o; o += up(P * s.d * 4);
     L.total = o;

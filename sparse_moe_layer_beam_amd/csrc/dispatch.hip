@@ -39,7 +39,8 @@ __device__ int block_excl_scan(int* buf, int* tmp, int n) {
 
 // Work tiles for the grouped GEMMs, expert-major: for every tile_m rows of each expert's
 // segment a record {expert, first row, index of the expert's first tile, tiles of the
-// expert}. cnt[] holds per-expert counts on entry (clobbered).
+// expert}; n_tiles[0] = the number of tiles, n_tiles[1 .. kTileWords-1] (the GEMMs' work-queue
+// counters) = 0. cnt[] holds per-expert counts on entry (clobbered).
 __device__ void write_tiles(int* cnt, int* tmp, int E, int tile_m, int32_t* tiles, int32_t* n_tiles) {
     const int t = threadIdx.x;
     int mt = 0;
@@ -58,6 +59,7 @@ __device__ void write_tiles(int* cnt, int* tmp, int E, int tile_m, int32_t* tile
             rec[3] = mt;
         }
     if (t == 0) *n_tiles = total;
+    else if (t < kTileWords) n_tiles[t] = 0;
 }
 
 // ---------------------------------------------------------------------------------------

@@ -444,7 +444,7 @@ bool experts_tiled(const Shape& s) { return gemm_supports(s) && s.T * (int64_t)s
 int experts_tile_m(const Shape& s) { return experts_tiled(s) ? gemm_tile_m() : 16 * kMT; }
 
 void launch_swiglu(const Shape& s, const void* x, const int32_t* offsets, const int32_t* sorted_pairs,
-                   const int32_t* tiles, const int32_t* n_tiles, const void* Wg, const void* Wu, void* h,
+                   const int32_t* tiles, int32_t* n_tiles, const void* Wg, const void* Wu, void* h,
                    hipStream_t st) {
     if (experts_tiled(s)) {
         launch_gemm_swiglu(s, x, offsets, sorted_pairs, tiles, n_tiles, Wg, Wu, h, st);
@@ -466,7 +466,7 @@ void launch_swiglu(const Shape& s, const void* x, const int32_t* offsets, const 
 }
 
 void launch_down(const Shape& s, const void* h, const int32_t* offsets, const int32_t* sorted_pairs,
-                 const float* topk_w, const int32_t* tiles, const int32_t* n_tiles, const void* Wd,
+                 const float* topk_w, const int32_t* tiles, int32_t* n_tiles, const void* Wd,
                  float* y_perm, hipStream_t st) {
     if (experts_tiled(s)) {
         launch_gemm_down(s, h, offsets, sorted_pairs, topk_w, tiles, n_tiles, Wd, y_perm, st);

@@ -184,16 +184,58 @@ __device__ __forceinline__ void gemm_run(u16* lds, const u16* const (&src)[DMA],
     }
 }
 
+// The block's work item. Each XCD owns the contiguous range [x*per_xcd, (x+1)*per_xcd) of the
+// item order and hands it out in order through its counter q[x]; a block whose XCD has spent
+// its range takes the next item of the range with the most items left, so that the XCDs end
+// together although their items differ in cost (tile fill). Returns -1 once every item has
+// been claimed: a claim that fails means its range is spent for good, so at most nine tries
+// are needed. Lane 0 of wave 0 claims; the result reaches the other waves through the first
+// LDS word, before any load into LDS is issued.
+__device__ __forceinline__ int claim_item(int32_t* q, int x, int per_xcd, int n_items, u16* lds) {
+    int32_t* const word = reinterpret_cast<int32_t*>(lds);
+    if (threadIdx.x == 0) {
+        int got = -1, y = x;
+        for (int tries = 0; tries < 16; ++tries) {
+            const int len = min(per_xcd, n_items - y * per_xcd);
+            if (len > 0) {
+                const int v = atomicAdd(q + y, 1);
+                if (v < len) {
+                    got = y * per_xcd + v;
+                    break;
+                }
+            }
+            int most = 0;
+            y = -1;
+            for (int z = 0; z < 8; ++z) {
+                const int left = min(per_xcd, n_items - z * per_xcd) -
+                                 __hip_atomic_load(q + z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (left > most) {
+                    most = left;
+                    y = z;
+                }
+            }
+            if (y < 0) break;
+        }
+        *word = got;
+    }
+    __syncthreads();
+    const int item = __builtin_amdgcn_readfirstlane(*reinterpret_cast<volatile int32_t*>(word));
+    __syncthreads();
+    return item;
+}
+
 // MODE 0: out = h [P, I] bf16 = bf16(silu(act . Wg^T) * (act . Wu^T)), act = x rows gathered
 //         through sorted_pairs (token = pair / top_k); W0 = Wg, W1 = Wu, both [E, Ndim, Kdim].
 // MODE 1: out = y_perm [P, d] fp32 = w_pair * (act . Wd^T), act = h rows in sorted order;
 //         W0 = Wd [E, Ndim, Kdim].
 // DENSE: one expert holding all act_rows tokens in order (the dense SwiGLU MLP): no tile
-//         list, no gather, weight 1; MODE 1 then writes y [T, d] directly.
+//         list, no gather, weight 1; MODE 1 then writes y [T, d] directly. Its items all cost
+//         the same and map to blocks statically; the grouped GEMMs claim theirs (claim_item)
+//         from the counters that follow the tile count in n_tiles_p.
 template <int MODE, bool DENSE, bool PK>
 __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(
         const u16* __restrict__ act, const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pairs,
-        const int32_t* __restrict__ tiles, const int32_t* __restrict__ n_tiles_p, const u16* __restrict__ W0,
+        const int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles_p, const u16* __restrict__ W0,
         const u16* __restrict__ W1, const float* __restrict__ topk_w, int top_k, void* __restrict__ out, int Kdim,
         int Ndim, int n_nb, int act_rows) {
     __shared__ __attribute__((aligned(1024))) u16 lds[NTB * TELEMS + NWB * WELEMS];
@@ -205,10 +247,16 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(
     const int n_mt_dense = (act_rows + GM - 1) / GM;
     const int n_items = DENSE ? n_mt_dense * n_nb : *n_tiles_p * n_nb;
     const int per_xcd = (n_items + 7) / 8;
-    const int slot = blockIdx.x >> 3;
-    if (slot >= per_xcd) return;
-    const int item = (blockIdx.x & 7) * per_xcd + slot;
-    if (item >= n_items) return;
+    int item;
+    if constexpr (DENSE) {
+        const int slot = blockIdx.x >> 3;
+        if (slot >= per_xcd) return;
+        item = (blockIdx.x & 7) * per_xcd + slot;
+        if (item >= n_items) return;
+    } else {
+        item = claim_item(n_tiles_p + 1 + 8 * MODE, blockIdx.x & 7, per_xcd, n_items, lds);
+        if (item < 0) return;
+    }
     int e, local, cnt, beg, n_e;
     if constexpr (DENSE) {
         e = 0;
@@ -335,7 +383,7 @@ bool gemm_supports(const Shape& s) {
 }
 
 void launch_gemm_swiglu(const Shape& s, const void* x, const int32_t* offsets, const int32_t* sorted_pairs,
-                        const int32_t* tiles, const int32_t* n_tiles, const void* Wg, const void* Wu, void* h,
+                        const int32_t* tiles, int32_t* n_tiles, const void* Wg, const void* Wu, void* h,
                         hipStream_t st) {
     const int n_nb = (s.I + GN / 2 - 1) / (GN / 2);
     const int blocks = (max_items(s, n_nb) + 7) / 8 * 8;
@@ -348,7 +396,7 @@ void launch_gemm_swiglu(const Shape& s, const void* x, const int32_t* offsets, c
 }
 
 void launch_gemm_down(const Shape& s, const void* h, const int32_t* offsets, const int32_t* sorted_pairs,
-                      const float* topk_w, const int32_t* tiles, const int32_t* n_tiles, const void* Wd,
+                      const float* topk_w, const int32_t* tiles, int32_t* n_tiles, const void* Wd,
                       float* y_perm, hipStream_t st) {
     const int n_nb = (s.d + GN - 1) / GN;
     const int blocks = (max_items(s, n_nb) + 7) / 8 * 8;

@@ -27,6 +27,9 @@ void launch_router(const Shape& s, const void* x, const float* Wr, const float* 
 
 // Dispatch (dispatch.hip)
 constexpr int kChunkPairs = 1024;
+// The tile count that the dispatch writes for the grouped GEMMs is followed by their work-queue
+// counters, one per XCD for each of the two GEMMs, which the same dispatch zeroes.
+constexpr int kTileWords = 1 + 2 * 8;
 void launch_dispatch(const Shape& s, const int32_t* idx, int32_t* offsets, int32_t* sorted_pairs,
                      int32_t* pair_rank, int32_t* chunk_counts, int32_t* rank_in_chunk, int32_t* tiles,
                      int32_t* n_tiles, int tile_m, hipStream_t st);
@@ -37,16 +40,16 @@ bool experts_tiled(const Shape& s);
 int gemm_tile_m();
 bool gemm_supports(const Shape& s);
 void launch_gemm_swiglu(const Shape& s, const void* x, const int32_t* offsets, const int32_t* sorted_pairs,
-                        const int32_t* tiles, const int32_t* n_tiles, const void* Wg, const void* Wu, void* h,
+                        const int32_t* tiles, int32_t* n_tiles, const void* Wg, const void* Wu, void* h,
                         hipStream_t st);
 void launch_gemm_down(const Shape& s, const void* h, const int32_t* offsets, const int32_t* sorted_pairs,
-                      const float* topk_w, const int32_t* tiles, const int32_t* n_tiles, const void* Wd,
+                      const float* topk_w, const int32_t* tiles, int32_t* n_tiles, const void* Wd,
                       float* y_perm, hipStream_t st);
 void launch_swiglu(const Shape& s, const void* x, const int32_t* offsets, const int32_t* sorted_pairs,
-                   const int32_t* tiles, const int32_t* n_tiles, const void* Wg, const void* Wu, void* h,
+                   const int32_t* tiles, int32_t* n_tiles, const void* Wg, const void* Wu, void* h,
                    hipStream_t st);
 void launch_down(const Shape& s, const void* h, const int32_t* offsets, const int32_t* sorted_pairs,
-                 const float* topk_w, const int32_t* tiles, const int32_t* n_tiles, const void* Wd, float* y_perm,
+                 const float* topk_w, const int32_t* tiles, int32_t* n_tiles, const void* Wd, float* y_perm,
                  hipStream_t st);
 void launch_combine(const Shape& s, const float* y_perm, const int32_t* pair_rank, float* y, hipStream_t st);
 
