@@ -209,7 +209,13 @@ __global__ __launch_bounds__(256) void swiglu_fp8_kernel(const u16* __restrict__
     }
 }
 
-// y_perm[beg+m, n] = w_pair * (h[beg+m] . Wd[e,n]) with fp8 Wd. grid: (ceil(d / 64), E).
+// y_perm[beg+m, n] = w_pair * (h[beg+m] . Wd[e,n]) with fp8 Wd. grid: (ceil(d / (64 * kDnRB)), E);
+// block: 4 waves, each streaming kDnRB blocks of 16 output channels whose rows share the
+// activation fragments (one 16-row block of 1-byte codes is only a 40 KB stream at I = 2560).
+#ifndef BEAM_FP8_DN_RB
+#define BEAM_FP8_DN_RB 2
+#endif
+constexpr int kDnRB = BEAM_FP8_DN_RB;
 template <bool PK>
 __global__ __launch_bounds__(256) void down_fp8_kernel(const u16* __restrict__ h, const int32_t* __restrict__ offsets,
                                                        const int32_t* __restrict__ sorted_pairs,
@@ -221,21 +227,29 @@ __global__ __launch_bounds__(256) void down_fp8_kernel(const u16* __restrict__ h
     const int n_e = offsets[e + 1] - beg;
     if (n_e <= 0) return;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int n0 = (blockIdx.x * kWaves + wave) * 16;
-    if (n0 >= d) return;
+    const int n0 = (blockIdx.x * kWaves + wave) * 16 * kDnRB;
+    if (n0 >= d) return;                                           // d % 512 == 0: all kDnRB blocks in range
     const int r = lane & 15, c = lane >> 4;
-    const size_t row = (size_t)e * d + n0 + r;
     for (int mb = 0; mb < n_e; mb += 16) {
         const u16* const hp[1] = {h + (size_t)(beg + min(mb + r, n_e - 1)) * I + 16 * c};
-        const size_t wo = PK ? (((size_t)e * d + n0) / 16 * (I / 64) * 64 + lane) * 16 : row * I + 16 * c;
-        const uint8_t* const wq[1] = {Wd + wo};
-        const uint8_t* const ws[1] = {sd + row * (I / 32)};
-        f32x4 acc[1][1] = {{{0, 0, 0, 0}}};
-        stream_fp8<1, 1, PK>(wq, ws, hp, I, c, acc);
+        const uint8_t* wq[kDnRB];
+        const uint8_t* ws[kDnRB];
+#pragma unroll
+        for (int b = 0; b < kDnRB; ++b) {
+            const size_t nb = (size_t)e * d + n0 + 16 * b, row = nb + r;
+            wq[b] = Wd + (PK ? (nb / 16 * (I / 64) * 64 + lane) * 16 : row * I + 16 * c);
+            ws[b] = sd + row * (I / 32);
+        }
+        f32x4 acc[1][kDnRB];
+#pragma unroll
+        for (int b = 0; b < kDnRB; ++b) acc[0][b] = f32x4{0, 0, 0, 0};
+        stream_fp8<kDnRB, 1, PK>(wq, ws, hp, I, c, acc);
         if (mb + r < n_e) {
             const float wt = topk_w[sorted_pairs[beg + mb + r]];
-            *reinterpret_cast<float4*>(y_perm + (size_t)(beg + mb + r) * d + n0 + 4 * c) =
-                make_float4(wt * acc[0][0][0], wt * acc[0][0][1], wt * acc[0][0][2], wt * acc[0][0][3]);
+#pragma unroll
+            for (int b = 0; b < kDnRB; ++b)
+                *reinterpret_cast<float4*>(y_perm + (size_t)(beg + mb + r) * d + n0 + 16 * b + 4 * c) =
+                    make_float4(wt * acc[0][b][0], wt * acc[0][b][1], wt * acc[0][b][2], wt * acc[0][b][3]);
         }
     }
 }
@@ -264,7 +278,8 @@ void launch_swiglu_fp8(const Shape& s, const void* x, const int32_t* offsets, co
 void launch_down_fp8(const Shape& s, const void* h, const int32_t* offsets, const int32_t* sorted_pairs,
                      const float* topk_w, const void* Wd8, const void* sd, float* y_perm, hipStream_t st) {
 #define BEAM_DN8(PK)                                                                                          \
-    hipLaunchKernelGGL((down_fp8_kernel<PK>), dim3((unsigned)((s.d + 63) / 64), (unsigned)s.E), dim3(256), 0, st,   \
+    hipLaunchKernelGGL((down_fp8_kernel<PK>), dim3((unsigned)((s.d + 64 * kDnRB - 1) / (64 * kDnRB)), (unsigned)s.E), \
+                       dim3(256), 0, st,                                                                      \
                        static_cast<const u16*>(h), offsets, sorted_pairs, topk_w, static_cast<const uint8_t*>(Wd8), \
                        static_cast<const uint8_t*>(sd), y_perm, s.d, s.I)
     if (s.packed) BEAM_DN8(true); else BEAM_DN8(false);
