@@ -10,6 +10,18 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint16_t u16;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// A 16-byte load of data that one call reads once (the expert weights the decode kernels
+// stream), with the non-temporal hint. Measured on MI355X, streams of 1 KB per load
+// instruction read ~6.7-7.0 TB/s with it and ~6.1 TB/s without.
+#ifndef BEAM_STREAM_NT
+#define BEAM_STREAM_NT 1
+#endif
+__device__ __forceinline__ u32x4 ld_once(const void* p) {
+    if constexpr (BEAM_STREAM_NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    else return *reinterpret_cast<const u32x4*>(p);
+}
 
 constexpr int kWave = 64;
 

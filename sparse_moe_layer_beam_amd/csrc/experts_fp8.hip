@@ -19,7 +19,6 @@
 namespace beam {
 namespace {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;
@@ -116,7 +115,10 @@ __device__ __forceinline__ bf16x8 widen(uint32_t lo, uint32_t hi, float sc) {
 template <int RB, int MT, bool PK>
 __device__ __forceinline__ void stream_fp8(const uint8_t* const (&wq)[RB], const uint8_t* const (&ws)[RB],
                                            const u16* const (&x)[MT], int K, int c, f32x4 (&acc)[MT][RB]) {
-    constexpr int kWB = PK ? 1024 : 64;                           // weight bytes from one step to the next
+    // weight bytes from one step to the next. Packed, a load reads a kilobyte that nothing else
+    // reads in the call (non-temporal hint); row-major, consecutive steps read the two halves of
+    // the same 128-byte lines (plain loads, which keep the line for the second half).
+    constexpr int kWB = PK ? 1024 : 64;
     u32x4 wa[kD][RB];
     bf16x8 xa[kD][MT][2];
     const int nsteps = K / 64;
@@ -130,7 +132,8 @@ __device__ __forceinline__ void stream_fp8(const uint8_t* const (&wq)[RB], const
 #pragma unroll
     for (int t = 0; t < kD; ++t) {
 #pragma unroll
-        for (int b = 0; b < RB; ++b) wa[t][b] = *reinterpret_cast<const u32x4*>(wq[b] + kWB * t);
+        for (int b = 0; b < RB; ++b)
+            wa[t][b] = PK ? ld_once(wq[b] + kWB * t) : *reinterpret_cast<const u32x4*>(wq[b] + kWB * t);
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
             xa[t][m][0] = *reinterpret_cast<const bf16x8*>(x[m] + 64 * t);
@@ -159,7 +162,8 @@ __device__ __forceinline__ void stream_fp8(const uint8_t* const (&wq)[RB], const
             const int tn = min(g + kD + t, last);                  // clamped: in bounds, unused at the end
             const int kn = 64 * tn;
 #pragma unroll
-            for (int b = 0; b < RB; ++b) wa[t][b] = *reinterpret_cast<const u32x4*>(wq[b] + (size_t)kWB * tn);
+            for (int b = 0; b < RB; ++b)
+                wa[t][b] = PK ? ld_once(wq[b] + (size_t)kWB * tn) : *reinterpret_cast<const u32x4*>(wq[b] + (size_t)kWB * tn);
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
                 xa[t][m][0] = *reinterpret_cast<const bf16x8*>(x[m] + kn);
