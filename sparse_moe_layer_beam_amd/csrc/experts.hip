@@ -31,7 +31,7 @@ namespace {
 #define BEAM_GU_DEPTH 6         // gate/up: k-steps of 32 prefetched ahead of the MFMAs
 #endif
 #ifndef BEAM_DN_DEPTH
-#define BEAM_DN_DEPTH 8         // down: the same
+#define BEAM_DN_DEPTH 6         // down: the same
 #endif
 #ifndef BEAM_GU_OCC
 #define BEAM_GU_OCC 3           // gate/up: blocks of 4 waves per CU the registers must allow
@@ -50,6 +50,9 @@ namespace {
 #endif
 
 constexpr int kWavesPerBlock = 4;
+// a block's waves cover whole k-split groups
+static_assert(BEAM_GU_KSPLIT >= 1 && kWavesPerBlock % BEAM_GU_KSPLIT == 0, "gate/up k split must divide 4 waves");
+static_assert(BEAM_DN_KSPLIT >= 1 && kWavesPerBlock % BEAM_DN_KSPLIT == 0, "down k split must divide 4 waves");
 constexpr int kDgu = BEAM_GU_DEPTH;
 constexpr int kDdn = BEAM_DN_DEPTH;
 constexpr int kMT = BEAM_STREAM_MT;
