@@ -254,6 +254,11 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(
         item = (blockIdx.x & 7) * per_xcd + slot;
         if (item >= n_items) return;
     } else {
+        // The grid is sized for the largest possible tile list. A block runs one item, so an XCD
+        // can take items from another only with blocks to spare: a quarter more blocks than items
+        // claim (the XCDs' shares of the work differ by up to ~16% at T=8192), the rest leave at
+        // once. A claim fails only once every item is claimed, so all items are taken.
+        if ((int)blockIdx.x >= n_items + n_items / 4 + 64) return;
         item = claim_item(n_tiles_p + 1 + 8 * MODE, blockIdx.x & 7, per_xcd, n_items, lds);
         if (item < 0) return;
     }

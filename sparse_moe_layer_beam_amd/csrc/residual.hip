@@ -22,6 +22,12 @@ namespace {
 
 __device__ __forceinline__ float4 add4(float4 a, float4 b) { return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w); }
 
+// A float4 of Y_perm, which the combine reads once (non-temporal).
+__device__ __forceinline__ float4 ld4_once(const float* p) {
+    const u32x4 r = ld_once(p);
+    return make_float4(__uint_as_float(r.x), __uint_as_float(r.y), __uint_as_float(r.z), __uint_as_float(r.w));
+}
+
 // COMBINE: src is Y_perm [T*K, d] read through pair_rank; else src is y [T, d].
 template <bool COMBINE, int kThreads>
 __global__ __launch_bounds__(kThreads) void post_residual_kernel(const float* __restrict__ src,
@@ -44,10 +50,10 @@ __global__ __launch_bounds__(kThreads) void post_residual_kernel(const float* __
         for (int i = 0; i < kMaxV; ++i) {
             const int q = tid + i * kThreads;
             if (q < nq) {
-                float4 acc = *reinterpret_cast<const float4*>(src + (size_t)rk[0] * d + 4 * q);
+                float4 acc = ld4_once(src + (size_t)rk[0] * d + 4 * q);
 #pragma unroll
                 for (int j = 1; j < 16; ++j)
-                    if (j < K) acc = add4(acc, *reinterpret_cast<const float4*>(src + (size_t)rk[j] * d + 4 * q));
+                    if (j < K) acc = add4(acc, ld4_once(src + (size_t)rk[j] * d + 4 * q));
                 v[i] = acc;
             }
         }
