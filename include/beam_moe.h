@@ -204,10 +204,10 @@ beam_moe_status beam_moe_forward_fp8(const beam_moe_shape* shape, const void* x,
  * first 3 layers use a dense SwiGLU MLP; BeamConfig: intermediate_size, hidden_act):
  *   y = Wd . bf16(silu(Wg . x) * (Wu . x))   per token, BF16 MFMA with FP32 accumulation,
  * h rounded to bf16 once as in the experts; no routing, no scaling.
- *   T, d, I    tokens, hidden size (5120), intermediate size (20480). T <= 64 (decode): d a
- *              multiple of 128 and I of 64; weight streams against the tokens, the reduction
- *              over k split in parts added in a fixed order. Otherwise the tiled GEMM, d and I
- *              multiples of 128. T*d, T*I and d*I below 2^31. Else BEAM_MOE_ERR_UNSUPPORTED_SHAPE.
+ *   T, d, I    tokens, hidden size (5120), intermediate size (20480); d and I multiples of
+ *              128, T*d, T*I and d*I below 2^31, else BEAM_MOE_ERR_UNSUPPORTED_SHAPE. T <= 64
+ *              (decode): weight streams against the tokens, the reduction over k split in parts
+ *              added in a fixed order. Larger T: the tiled GEMM.
  *   weight_layout  BEAM_MOE_WEIGHTS_ROW_MAJOR, or PACKED (Wg, Wu through beam_moe_pack_weights
  *              as [I, d], Wd as [d, I]); else BEAM_MOE_ERR_INVALID_ARG. Same results either way.
  *   x          [T, d] bf16

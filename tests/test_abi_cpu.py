@@ -180,7 +180,8 @@ def test_dense_mlp_validates_before_launching():
     assert f(64, 5120, 20480, None, A, A, A, A, WS(n)) == INVALID          # x missing
     assert f(64, 5120, 20480, A, A, A, A, A + 4, WS(n)) == INVALID         # misaligned y
     assert f(65, 5120 + 64, 20480, A, A, A, A, A, WS(n)) == UNSUPPORTED    # GEMM path: d not a multiple of 128
-    assert f(64, 5120 + 32, 20480, A, A, A, A, A, WS(n)) == UNSUPPORTED    # stream path: d not a multiple of 64
+    assert f(64, 5120 + 32, 20480, A, A, A, A, A, WS(n)) == UNSUPPORTED    # stream path: d not a multiple of 128
+    assert f(64, 5120, 20480 + 64, A, A, A, A, A, WS(n)) == UNSUPPORTED    # stream path: I not a multiple of 128
     assert moe.beam_moe_dense_mlp(64, 5120, 20480, A, A, A, A, A, WS(n), weight_layout=2, stream=0,
                                   check=False) == INVALID
     assert f(-3, 5120, 20480, A, A, A, A, A, WS(n)) == INVALID
