@@ -15,8 +15,9 @@
 // Weights come row-major ([E, I, d] gate/up, [E, d, I] down) or in the packed layout of
 // beam_moe_pack_weights: 16-row blocks stored as runs of 32-k steps, each step the 1 KB a
 // wave loads (lane l: row l % 16, k 8(l / 16) .. +8). Row-major, one load instruction reads
-// 64 bytes from each of 16 rows; packed, it reads 1 KB that is contiguous, and the stream
-// runs at 6.2-6.3 TB/s instead of 5.6 on MI355X (same values, bitwise-equal results).
+// 64 bytes from each of 16 rows; packed, it reads 1 KB that is contiguous and that nothing else
+// in the call reads, so it takes the non-temporal hint, and the stream runs at 6.8-7.0 TB/s
+// instead of 5.6 on MI355X (same values, bitwise-equal results).
 //
 // Also here: the packing kernel itself, and the dense SwiGLU MLP for decode-sized batches
 // (Transformers "Beam" page, Overview: the first 3 layers use a dense MLP), which streams its
@@ -327,8 +328,8 @@ __global__ __launch_bounds__(256) void pack_stream_kernel(const u16* __restrict_
 // wave's token fragments are contiguous kilobytes like its weight fragments. In both kernels
 // the 4 waves of a block stream the same weight rows over four consecutive parts of k against
 // the four tiles, and their sums meet in LDS, added in part order. Measured on MI355X at
-// d = 5120, I = 20480: gate/up with its SwiGLU in the same kernel 11% faster than k parts
-// added by a second kernel (the gate/up time of the layer 0.187 -> 0.166 ms).
+// T = 64, d = 5120, I = 20480: 0.161 ms, against 0.190 ms with every k part written out and
+// added by a second kernel.
 constexpr int kDT = 4;                   // token tiles (64 tokens)
 constexpr int kDD = 3;                   // ring depth of the dense streams
 constexpr int kDenseKsDN = 8;            // most k parts of the down pass across blocks
