@@ -59,7 +59,7 @@ Layout layout(const Shape& s) {
     size_t o = 0;
     L.xn = o; o += up(T * s.d * 2);
     L.wrs = o; o += up(beam::router_split_bytes(s));
-    L.zp = o; o += up((size_t)beam::router_ksplit(s) * T * s.E * 4);
+    L.zp = o; o += up(beam::router_zp_floats(s) * 4);
     L.idx = o; o += up(P * 4);
     L.w = o; o += up(P * 4);
     L.cc = o; o += up(n_chunks * s.E * 4);

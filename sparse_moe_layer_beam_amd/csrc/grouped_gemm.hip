@@ -228,8 +228,10 @@ __device__ __forceinline__ int claim_item(int32_t* q, int x, int per_xcd, int n_
 //         through sorted_pairs (token = pair / top_k); W0 = Wg, W1 = Wu, both [E, Ndim, Kdim].
 // MODE 1: out = y_perm [P, d] fp32 = w_pair * (act . Wd^T), act = h rows in sorted order;
 //         W0 = Wd [E, Ndim, Kdim].
-// DENSE: one expert holding all act_rows tokens in order (the dense SwiGLU MLP): no tile
-//         list, no gather, weight 1; MODE 1 then writes y [T, d] directly. Its items all cost
+// DENSE: one expert holding all act_rows tokens in order (the dense SwiGLU MLP, the router
+//         logits): no tile list, no gather, weight 1; MODE 1 then writes y [T, Ndim] directly.
+//         k may be cut into kparts parts of Kdim (rows ldk long); part kb writes its partial
+//         product to out + kb * act_rows * Ndim. Its items all cost
 //         the same and map to blocks statically; the grouped GEMMs claim theirs (claim_item)
 //         from the counters that follow the tile count in n_tiles_p.
 template <int MODE, bool DENSE, bool PK>
@@ -237,7 +239,7 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(
         const u16* __restrict__ act, const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pairs,
         const int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles_p, const u16* __restrict__ W0,
         const u16* __restrict__ W1, const float* __restrict__ topk_w, int top_k, void* __restrict__ out, int Kdim,
-        int Ndim, int n_nb, int act_rows) {
+        int Ndim, int n_nb, int act_rows, int ldk, int kparts) {
     __shared__ __attribute__((aligned(1024))) u16 lds[NTB * TELEMS + NWB * WELEMS];
 
     // Work item -> (expert, n-block, m-tile). Blocks are dispatched to the 8 XCDs round-robin
@@ -245,7 +247,7 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(
     // contiguous item range [x*per_xcd, (x+1)*per_xcd), expert-major, so the items sharing
     // one expert's weights and tokens run together on one XCD.
     const int n_mt_dense = (act_rows + GM - 1) / GM;
-    const int n_items = DENSE ? n_mt_dense * n_nb : *n_tiles_p * n_nb;
+    const int n_items = DENSE ? n_mt_dense * n_nb * kparts : *n_tiles_p * n_nb;
     const int per_xcd = (n_items + 7) / 8;
     int item;
     if constexpr (DENSE) {
@@ -262,10 +264,11 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(
         item = claim_item(n_tiles_p + 1 + 8 * MODE, blockIdx.x & 7, per_xcd, n_items, lds);
         if (item < 0) return;
     }
-    int e, local, cnt, beg, n_e;
+    int e, local, cnt, beg, n_e, kb = 0;
     if constexpr (DENSE) {
+        kb = item / (n_mt_dense * n_nb);
         e = 0;
-        local = item;
+        local = item - kb * (n_mt_dense * n_nb);
         cnt = n_mt_dense;
         beg = 0;
         n_e = act_rows;
@@ -310,7 +313,7 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(
             size_t tr;
             if constexpr (MODE == 0 && !DENSE) tr = (size_t)(sorted_pairs[beg + m] / top_k);
             else tr = (size_t)(beg + m);
-            p = act + tr * Kdim;
+            p = act + tr * ldk + (size_t)kb * Kdim;
         } else if constexpr (PK) {
             // weight wave ww loads 16-row blocks 4ww .. 4ww+3 of the tile, two 32-k steps each
             const int qb = 4 * (wave - NW / 2) + i / 2;
@@ -323,7 +326,7 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(
                 ch = n0 + 16 * qb;
             }
             const size_t blk = ((size_t)e * Ndim + min(ch, Ndim - 16)) / 16;   // past Ndim: the last block
-            src[i] = W + (blk * (Kdim / 32) * 64 + lane) * 8 + (i % 2) * 512;
+            src[i] = W + (blk * (ldk / 32) * 64 + lane) * 8 + (size_t)kb * Kdim * 16 + (i % 2) * 512;
             continue;
         } else {
             const int wr = row - GM;
@@ -335,7 +338,7 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(
             } else {
                 ch = n0 + wr;
             }
-            p = W + ((size_t)e * Ndim + min(ch, Ndim - 1)) * Kdim;
+            p = W + ((size_t)e * Ndim + min(ch, Ndim - 1)) * ldk + (size_t)kb * Kdim;
         }
         src[i] = p + 8 * chunk;
     }
@@ -362,6 +365,7 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(
     const int nstages = Kdim / GK;
     const size_t orow0 = (size_t)(beg + m0);
     const int32_t* pair_of_row = DENSE ? nullptr : sorted_pairs + beg + m0;
+    if constexpr (MODE == 1 && DENSE) out = static_cast<float*>(out) + (size_t)kb * act_rows * Ndim;
     switch (live) {
 #define BEAM_GEMM_CASE(L)                                                                                     \
     case L:                                                                                                   \
@@ -395,7 +399,7 @@ void launch_gemm_swiglu(const Shape& s, const void* x, const int32_t* offsets, c
 #define BEAM_GU(PK)                                                                                           \
     hipLaunchKernelGGL((grouped_gemm_kernel<0, false, PK>), dim3((unsigned)blocks), dim3(NT), 0, st,           \
                        (const u16*)x, offsets, sorted_pairs, tiles, n_tiles, (const u16*)Wg, (const u16*)Wu,  \
-                       nullptr, s.K, h, s.d, s.I, n_nb, (int)s.T)
+                       nullptr, s.K, h, s.d, s.I, n_nb, (int)s.T, s.d, 1)
     if (s.packed) BEAM_GU(true); else BEAM_GU(false);
 #undef BEAM_GU
 }
@@ -408,7 +412,7 @@ void launch_gemm_down(const Shape& s, const void* h, const int32_t* offsets, con
 #define BEAM_DN(PK)                                                                                           \
     hipLaunchKernelGGL((grouped_gemm_kernel<1, false, PK>), dim3((unsigned)blocks), dim3(NT), 0, st,           \
                        (const u16*)h, offsets, sorted_pairs, tiles, n_tiles, (const u16*)Wd, nullptr, topk_w, \
-                       s.K, y_perm, s.I, s.d, n_nb, (int)(s.T * s.K))
+                       s.K, y_perm, s.I, s.d, n_nb, (int)(s.T * s.K), s.I, 1)
     if (s.packed) BEAM_DN(true); else BEAM_DN(false);
 #undef BEAM_DN
 }
@@ -422,7 +426,7 @@ void launch_dense_swiglu(int64_t T, int d, int I, bool packed, const void* x, co
 #define BEAM_DGU(PK)                                                                                          \
     hipLaunchKernelGGL((grouped_gemm_kernel<0, true, PK>), dim3((unsigned)((items + 7) / 8 * 8)), dim3(NT), 0, st, \
                        (const u16*)x, nullptr, nullptr, nullptr, nullptr, (const u16*)Wg, (const u16*)Wu, nullptr, 1, \
-                       h, d, I, n_nb, (int)T)
+                       h, d, I, n_nb, (int)T, d, 1)
     if (packed) BEAM_DGU(true); else BEAM_DGU(false);
 #undef BEAM_DGU
 }
@@ -433,9 +437,24 @@ void launch_dense_down(int64_t T, int d, int I, bool packed, const void* h, cons
 #define BEAM_DDN(PK)                                                                                          \
     hipLaunchKernelGGL((grouped_gemm_kernel<1, true, PK>), dim3((unsigned)((items + 7) / 8 * 8)), dim3(NT), 0, st, \
                        (const u16*)h, nullptr, nullptr, nullptr, nullptr, (const u16*)Wd, nullptr, nullptr, 1, y, I, d, \
-                       n_nb, (int)T)
+                       n_nb, (int)T, I, 1)
     if (packed) BEAM_DDN(true); else BEAM_DDN(false);
 #undef BEAM_DDN
+}
+
+// Router logits on the GEMM: zp[kb][t][pl*E + e] = x_t . WrS[pl][e] over k part kb of ks, for
+// the three bf16 planes pl of the split router weight ([3E, d], row-major).
+void launch_gemm_router(const Shape& s, const void* x, const void* WrS, float* zp, int ks, hipStream_t st) {
+    const int Ndim = 3 * s.E;
+    const int n_nb = (Ndim + GN - 1) / GN;
+    const int items = (int)((s.T + GM - 1) / GM) * n_nb * ks;
+    hipLaunchKernelGGL((grouped_gemm_kernel<1, true, false>), dim3((unsigned)((items + 7) / 8 * 8)), dim3(NT), 0, st,
+                       (const u16*)x, nullptr, nullptr, nullptr, nullptr, (const u16*)WrS, nullptr, nullptr, 1, zp,
+                       s.d / ks, Ndim, n_nb, (int)s.T, s.d, ks);
+}
+
+int gemm_router_items(const Shape& s, int ks) {
+    return (int)((s.T + GM - 1) / GM) * ((3 * s.E + GN - 1) / GN) * ks;
 }
 
 bool dense_supports(int64_t T, int d, int I) {

@@ -20,8 +20,9 @@ struct Shape {
 void launch_rmsnorm(const Shape& s, const void* h, const void* w, void* x_out, hipStream_t st);
 int router_ksplit(const Shape& s);
 size_t router_split_bytes(const Shape& s);
+size_t router_zp_floats(const Shape& s);
 // Logits, sigmoid, bias, group-limited top-k and weights for T tokens (x already normed).
-// wrs: scratch of router_split_bytes(s); z_part: scratch of router_ksplit(s) * T * E floats.
+// wrs: scratch of router_split_bytes(s); z_part: scratch of router_zp_floats(s) floats.
 void launch_router(const Shape& s, const void* x, const float* Wr, const float* bias, void* wrs, float* z_part,
                    int32_t* idx, float* w, float* logits, hipStream_t st);
 
@@ -38,6 +39,10 @@ void launch_dispatch(const Shape& s, const int32_t* idx, int32_t* offsets, int32
 int experts_tile_m(const Shape& s);
 bool experts_tiled(const Shape& s);
 int gemm_tile_m();
+// Router logits of large batches on the tiled GEMM (grouped_gemm.hip): zp[kb][t][pl*E + e]
+// over k part kb of ks, for the three planes pl of the split router weight.
+void launch_gemm_router(const Shape& s, const void* x, const void* WrS, float* zp, int ks, hipStream_t st);
+int gemm_router_items(const Shape& s, int ks);
 bool gemm_supports(const Shape& s);
 void launch_gemm_swiglu(const Shape& s, const void* x, const int32_t* offsets, const int32_t* sorted_pairs,
                         const int32_t* tiles, int32_t* n_tiles, const void* Wg, const void* Wu, void* h,

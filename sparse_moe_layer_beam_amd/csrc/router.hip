@@ -201,13 +201,14 @@ __device__ __forceinline__ void select_token(const float (&z)[EPL], int lane, in
     }
 }
 
-// Selection from K-split partial logits zp [ks][T][E]: one wavefront per token; the ks
-// partial sums of each logit are added in ascending split order (deterministic).
+// Selection from partial logits zp [ks][T][P*E] (P = 1, or 3 for the planes of the split
+// weight, which the GEMM route keeps apart): one wavefront per token; the ks*P partial sums of
+// each logit are added in ascending order of (k part, plane) (deterministic).
 template <int EPL>
 __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ zp, int ks, int64_t T, int E,
                                                           int G, int KG, int K, float S, int norm,
                                                           const float* __restrict__ bias, int32_t* __restrict__ idx,
-                                                          float* __restrict__ wout, float* __restrict__ logits) {
+                                                          float* __restrict__ wout, float* __restrict__ logits, int P) {
     const int lane = threadIdx.x & 63;
     const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
@@ -216,26 +217,28 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
 #pragma unroll
     for (int i = 0; i < EPL; ++i) z[i] = 0.0f;
     if (e0 < E) {
+        // part j = (k part, plane) of a logit row: j / P, j % P
+        const int parts = ks * P;
+        auto at = [&](int j) { return zp + ((int64_t)(j / P) * T + t) * (P * E) + (j % P) * E + e0; };
         if constexpr (EPL == 4) {
             // E is a multiple of 64 here, so each lane's 4 logits are one aligned float4
-            int q = 0;
-            for (; q + 8 <= ks; q += 8) {
+            int j = 0;
+            for (; j + 8 <= parts; j += 8) {
                 float4 v[8];
 #pragma unroll
-                for (int u = 0; u < 8; ++u)
-                    v[u] = *reinterpret_cast<const float4*>(zp + ((int64_t)(q + u) * T + t) * E + e0);
+                for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const float4*>(at(j + u));
 #pragma unroll
                 for (int u = 0; u < 8; ++u) { z[0] += v[u].x; z[1] += v[u].y; z[2] += v[u].z; z[3] += v[u].w; }
             }
-            for (; q < ks; ++q) {
-                const float4 v = *reinterpret_cast<const float4*>(zp + ((int64_t)q * T + t) * E + e0);
+            for (; j < parts; ++j) {
+                const float4 v = *reinterpret_cast<const float4*>(at(j));
                 z[0] += v.x; z[1] += v.y; z[2] += v.z; z[3] += v.w;
             }
         } else {
 #pragma unroll
             for (int i = 0; i < EPL; ++i)
                 if (e0 + i < E)
-                    for (int q = 0; q < ks; ++q) z[i] += zp[((int64_t)q * T + t) * E + e0 + i];
+                    for (int j = 0; j < parts; ++j) z[i] += at(j)[i];
         }
     }
     select_token<EPL>(z, lane, E, G, KG, K, S, norm, bias, idx + t * K, wout + t * K, logits ? logits + t * E : nullptr);
@@ -415,12 +418,41 @@ int router_ksplit(const Shape& s) {
 
 size_t router_split_bytes(const Shape& s) { return router_uses_mfma(s) ? (size_t)3 * s.E * s.d * 2 : 0; }
 
+// Large batches take the router product to the tiled GEMM (direct-to-LDS operand loads, 256 x
+// 256 tiles): the 64-token blocks of router_mfma_kernel each reload all 3E rows of the split
+// weight in MFMA operand layout, which bounds them by the L2-to-CU load rate. k is cut into the
+// fewest parts (of 1, 2, 4, 8) that give at least two items per CU. 0: not this route.
+#ifndef BEAM_ROUTER_GEMM_MIN_T
+#define BEAM_ROUTER_GEMM_MIN_T 2048
+#endif
+#ifndef BEAM_ROUTER_GEMM_ITEMS
+#define BEAM_ROUTER_GEMM_ITEMS 512
+#endif
+int router_gemm_ks(const Shape& s) {
+    if (!router_uses_mfma(s) || s.T < BEAM_ROUTER_GEMM_MIN_T || s.d % 128 != 0) return 0;
+    int ks = 1;
+    while (ks < 8 && gemm_router_items(s, ks) < BEAM_ROUTER_GEMM_ITEMS && s.d % (64 * 2 * ks) == 0) ks *= 2;
+    return ks;
+}
+
+size_t router_zp_floats(const Shape& s) {
+    const int gks = router_gemm_ks(s);
+    if (gks) return (size_t)gks * s.T * 3 * s.E;
+    return (size_t)router_ksplit(s) * s.T * s.E;
+}
+
 void launch_router(const Shape& s, const void* x, const float* Wr, const float* bias, void* wrs, float* z_part,
                    int32_t* idx, float* w, float* logits, hipStream_t st) {
-    const int ks = router_ksplit(s);
+    const int gks = router_gemm_ks(s);
+    const int ks = gks ? gks : router_ksplit(s);
+    const int P = gks ? 3 : 1;
     const int epl = s.E <= 64 ? 1 : s.E / 64;
     const unsigned tb = (unsigned)((s.T + 63) / 64);
-    if (router_uses_mfma(s)) {
+    if (gks) {
+        hipLaunchKernelGGL(router_split_kernel, dim3((unsigned)(s.d / 64), (unsigned)(s.E / 64)), dim3(256), 0, st,
+                           Wr, (u16*)wrs, s.d, s.E);
+        launch_gemm_router(s, x, wrs, z_part, gks, st);
+    } else if (router_uses_mfma(s)) {
         hipLaunchKernelGGL(router_split_kernel, dim3((unsigned)(s.d / 64), (unsigned)(s.E / 64)), dim3(256), 0, st,
                            Wr, (u16*)wrs, s.d, s.E);
 #define BEAM_RMMA(NTW, F)                                                                                        \
@@ -441,7 +473,7 @@ void launch_router(const Shape& s, const void* x, const float* Wr, const float* 
     dim3 grid((unsigned)((s.T + 3) / 4));
 #define BEAM_TOPK(N)                                                                                              \
     hipLaunchKernelGGL(router_topk_kernel<N>, grid, dim3(256), 0, st, z_part, ks, s.T, s.E, s.G, s.KG, s.K, s.S,  \
-                       s.norm, bias, idx, w, logits)
+                       s.norm, bias, idx, w, logits, P)
     switch (epl) {
         case 1: BEAM_TOPK(1); break;
         case 2: BEAM_TOPK(2); break;

@@ -42,6 +42,11 @@ SMALL = {
     # d not a multiple of 128: many tokens per expert but no tiled GEMM, so the weight streams
     # run 16-token tile after tile
     "d192_T500": Workload(34, "d192_T500", T=500, d=192, E=16, n_group=4, topk_group=2, top_k=4, I=192),
+    # from T = 2048 the router product runs on the tiled GEMM, k cut into parts: d = 512 gives
+    # eight one-stage parts; E = 128 leaves the second 256-row block of its 384 weight rows
+    # half past the end
+    "mid_T2100": Workload(35, "mid_T2100", T=2100, **_MID),
+    "e128_T2100": Workload(36, "e128_T2100", T=2100, d=256, E=128, n_group=4, topk_group=2, top_k=6, I=128),
 }
 BEAM = {i: recipes.WORKLOADS[i] for i in (1, 2, 3, 4)}
 
