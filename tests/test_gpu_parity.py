@@ -250,6 +250,29 @@ def test_identical_experts_beam_decode():
     assert err <= P.Y_TOL * rms
 
 
+@pytest.mark.parametrize("name", ["mid_T77", "mid_T2000"])
+def test_doubled_down_projection_doubles_y(name):
+    """Wd -> 2 Wd (exact in bf16) doubles y bit for bit: the routing does not see Wd, and every
+    product and sum after it scales by a power of two. T=77 runs the weight streams, T=2000 the
+    tiled GEMM; both on row-major and on packed weights."""
+    w = SMALL[name]
+    print("case doubled Wd", name, flush=True)
+    t = synth.device_inputs(w)
+    g = _gpu_forward(w, t)
+    t2 = dict(t)
+    t2["Wd"] = t["Wd"] * 2
+    g2 = _gpu_forward(w, t2)
+    assert np.array_equal(g2["idx"], g["idx"])
+    assert np.isfinite(g["y"]).all()
+    assert np.array_equal(g2["y"].view(np.uint32), (2 * g["y"]).view(np.uint32))
+    shape = moe.make_shape(w.T, w.d, w.E, w.n_group, w.topk_group, w.top_k, w.I, w.scale, w.norm_topk_prob, w.eps,
+                           weight_layout=moe.WEIGHTS_PACKED)
+    t3 = dict(t2)
+    t3["Wg"], t3["Wu"], t3["Wd"] = moe.pack_expert_weights(t["Wg"], t["Wu"], t2["Wd"])
+    g3 = _gpu_forward(w, t3, shape)
+    assert np.array_equal(g3["y"].view(np.uint32), g2["y"].view(np.uint32))
+
+
 def test_token_permutation_equivariance():
     """Permuting tokens permutes y bit for bit (no cross-token arithmetic)."""
     w = SMALL["mid_T2000"]
