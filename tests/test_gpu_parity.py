@@ -114,11 +114,33 @@ def test_synth_device_matches_host():
     assert np.array_equal(buf.cpu().numpy(), synth.host_uniform(4096, 7, recipes.TID_BIAS, -0.1, 0.1, synth.F32))
 
 
-@pytest.mark.parametrize("name", list(SMALL))
-def test_forward_parity_small(name):
-    """Whole layer on every token: routing, weights, logits and y against the oracle."""
-    w = SMALL[name]
-    print("case", name, flush=True)
+def _random_workload(i):
+    """A seeded random shape from the whole supported range (include/beam_moe.h): E up to 64
+    with power-of-two group sizes, or E in {128, 256, 512} with power-of-two group counts; any
+    topk_group and top_k they allow; d, I multiples of 64; ragged T (past 2048 the router runs on
+    the tiled GEMM); random scale, normalisation, pre-norm and hot experts."""
+    rng = np.random.default_rng(4242 + i)
+    E = int(rng.choice([8, 16, 24, 32, 48, 64, 128, 256, 512]))
+    if E <= 64:
+        gsz = int(rng.choice([g for g in (2, 4, 8, 16, 32, 64) if E % g == 0]))
+        G = E // gsz
+    else:
+        G = int(rng.choice([g for g in (1, 2, 4, 8, 16, 32, 64) if E // g >= 2]))
+    KG = int(rng.integers(1, G + 1))
+    K = int(rng.integers(1, min(16, KG * (E // G)) + 1))
+    d = int(rng.choice([64, 128, 192, 256, 384, 512]))
+    I = int(rng.choice([64, 128, 192, 256]))
+    T = int(rng.choice([1, 2, 7, 16, 33, 64, 65, 100, 255, 256, 257, 511, 700, 1200, 2100]))
+    while T * K > 12000:
+        T //= 2
+    hot = int(rng.integers(0, E // 4 + 1)) if rng.random() < 0.3 else 0
+    return Workload(60 + i, "random_%d" % i, T=T, d=d, E=E, n_group=G, topk_group=KG, top_k=K, I=I,
+                    scale=float(rng.uniform(0.5, 3.0)), norm_topk_prob=bool(rng.random() < 0.7),
+                    hot_experts=hot, hot_bias=0.3 if hot else 0.0, prenorm=bool(rng.random() < 0.3))
+
+
+def _check_every_token(w, name):
+    print("case", name, w, flush=True)
     t = synth.device_inputs(w)
     g = _gpu_forward(w, t)
     x, Wr, b = _oracle_inputs(w)
@@ -133,6 +155,18 @@ def test_forward_parity_small(name):
     print("%s: excused %d, max|dy| %.3e, rms %.3e" % (name, (~same).sum(), err, rms))
     assert np.isfinite(g["y"]).all()
     assert err <= P.Y_TOL * rms
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_forward_parity_small(name):
+    """Whole layer on every token: routing, weights, logits and y against the oracle."""
+    _check_every_token(SMALL[name], name)
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_forward_parity_random_shape(i):
+    """Whole layer on every token at a seeded random supported shape."""
+    _check_every_token(_random_workload(i), "random_%d" % i)
 
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4])
