@@ -15,7 +15,7 @@ import sparse_moe_layer_beam_amd as moe
 from synth import recipes
 from synth.recipes import Workload
 from tests import _parity as P
-from tests.test_gpu_parity import _shape, _oracle_inputs
+from tests.test_gpu_parity import _shape, _oracle_inputs, _random_workload
 
 pytestmark = pytest.mark.gpu
 
@@ -101,10 +101,24 @@ def _fp8_experts(w, ids):
     return out
 
 
-@pytest.mark.parametrize("cfg", ["mid", 1])
+def _random_fp8_workload(i):
+    """A seeded random supported shape, with d and I multiples of 512 (the FP8 kernels' k steps)
+    and few enough tokens per expert for the weight streams."""
+    from dataclasses import replace
+    rng = np.random.default_rng(777 + i)
+    w = _random_workload(i)
+    T = min(w.T, max(1, 16 * w.E // w.top_k))
+    return replace(w, cfg_id=80 + i, name="random_fp8_%d" % i, T=T, d=int(rng.choice([512, 1024])),
+                   I=int(rng.choice([512, 1024])))
+
+
+@pytest.mark.parametrize("cfg", ["mid", 1] + ["random_%d" % i for i in range(4)])
 def test_forward_fp8_parity(cfg):
-    w = MID if cfg == "mid" else recipes.WORKLOADS[cfg]
-    print("case forward_fp8", w.name, flush=True)
+    if isinstance(cfg, str) and cfg.startswith("random_"):
+        w = _random_fp8_workload(int(cfg.split("_")[1]))
+    else:
+        w = MID if cfg == "mid" else recipes.WORKLOADS[cfg]
+    print("case forward_fp8", w.name, w, flush=True)
     t = synth.device_inputs(w)
     y, idx, wt, y_bf16 = _gpu_fp8_forward(w, t)
     del t
@@ -114,7 +128,7 @@ def test_forward_fp8_parity(cfg):
     same = P.compare_routing(idx, wt, idx_ref, w_ref, gap, z_ref, b, w.n_group, w.topk_group, w.top_k)
     # every token at the mid shape; at the Beam shape a sample (each token's 8 experts are
     # generated, quantized and run on the host)
-    rows = np.arange(w.T) if w.d <= 512 else P.sample_tokens(idx_ref, n_extra=6, seed=7)
+    rows = np.arange(w.T) if w.d <= 1024 else P.sample_tokens(idx_ref, n_extra=6, seed=7)
     rows = np.array([r for r in rows if same[r]])
     experts = _fp8_experts(w, np.unique(idx_ref[rows]))
     y_ref = oracle.moe_rows(x[rows], idx_ref[rows], w_ref[rows], experts, w.E)

@@ -14,7 +14,7 @@ import synth
 import sparse_moe_layer_beam_amd as moe
 from synth import recipes
 from tests import _parity as P
-from tests.test_gpu_parity import SMALL, _gpu_forward, _oracle_inputs, _experts_host, _shape
+from tests.test_gpu_parity import SMALL, _gpu_forward, _oracle_inputs, _experts_host, _shape, _random_workload
 
 pytestmark = pytest.mark.gpu
 
@@ -49,10 +49,14 @@ def _free_gpu():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("name", ["tiny", "mid_T77", "mid_T2000", "e64_T150"])
+@pytest.mark.parametrize("name", ["tiny", "mid_T77", "mid_T2000", "e64_T150"] + ["random_%d" % i for i in range(4)])
 def test_share_small_every_token(name):
-    w = SMALL[name]
-    print("case share", name, flush=True)
+    if name.startswith("random_"):      # the share takes the layer's input x as it is: no pre-norm
+        from dataclasses import replace
+        w = replace(_random_workload(int(name.split("_")[1])), prenorm=False)
+    else:
+        w = SMALL[name]
+    print("case share", name, w, flush=True)
     t = synth.device_inputs(w)
     shape = _shape(w)
     full = _gpu_forward(w, t, shape)
