@@ -44,7 +44,11 @@ constexpr int TELEMS = GM * GK;          // bf16 of one token buffer (32 KB)
 constexpr int WELEMS = GN * GK;          // bf16 of one weight buffer (32 KB)
 constexpr int NTB = 2, NWB = 3;          // token and weight buffers: 160 KB of LDS
 constexpr int DMA = SROWS / (8 * NW);    // direct loads per wave per stage (8 rows each)
-constexpr int kFrag = 4;                 // token fragments read ahead of the MFMAs
+#ifndef BEAM_GEMM_KFRAG
+#define BEAM_GEMM_KFRAG 2
+#endif
+// token fragments read from LDS ahead of their MFMAs (2: ~1% faster than 4 on MI355X, 6 and 8 slower)
+constexpr int kFrag = BEAM_GEMM_KFRAG;
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
