@@ -36,7 +36,7 @@ def _setup(w, layout):
     return t, args, y
 
 
-@pytest.mark.parametrize("name,layout", [("beam1", 1), ("mid_T2000", 0), ("mid_prenorm_T333", 1)])
+@pytest.mark.parametrize("name,layout", [("beam1", 1), ("mid_T2000", 0), ("mid_T2100", 1), ("mid_prenorm_T333", 1)])
 def test_graph_replay_matches_eager(name, layout):
     w = recipes.WORKLOADS[1] if name == "beam1" else SMALL[name]
     print("case graph", name, layout, flush=True)
