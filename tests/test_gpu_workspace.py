@@ -90,3 +90,35 @@ def test_share_and_dense_ignore_workspace_contents():
             torch.cuda.synchronize()
             outs.append(yd.cpu().numpy())
         _same(outs)
+
+
+def test_two_layers_on_two_streams_at_once():
+    """No state outside the caller's workspace: two layers (weight streams and tiled GEMM paths)
+    launched concurrently on two streams, with their own workspaces, give the same bits as each
+    run alone."""
+    cases = []
+    for name, layout in (("mid_T77", 1), ("mid_T2000", 1)):
+        w = SMALL[name]
+        t = synth.device_inputs(w)
+        shape = moe.make_shape(w.T, w.d, w.E, w.n_group, w.topk_group, w.top_k, w.I, w.scale, w.norm_topk_prob,
+                               w.eps, weight_layout=layout)
+        W = moe.pack_expert_weights(t["Wg"], t["Wu"], t["Wd"]) if layout else (t["Wg"], t["Wu"], t["Wd"])
+        ws = torch.empty(moe.beam_moe_workspace_bytes(shape), dtype=torch.uint8, device="cuda")
+        y = torch.empty((w.T, w.d), dtype=torch.float32, device="cuda")
+        hid = t["h"] if w.prenorm else t["x"]
+        cases.append(((shape, hid, t.get("norm_w"), t["Wr"], t["bias"], *W, y, None, None, None, ws), y, t))
+    alone = []
+    for args, y, _ in cases:
+        moe.beam_moe_forward(*args)
+        torch.cuda.synchronize()
+        alone.append(y.clone())
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for rep in range(3):
+        for _, y, _ in cases:
+            y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        for (args, _, _), st in zip(cases, streams):
+            moe.beam_moe_forward(*args, stream=st.cuda_stream)
+        torch.cuda.synchronize()
+        for (_, y, _), ref in zip(cases, alone):
+            assert torch.equal(y, ref), "concurrent run %d differs" % rep
