@@ -313,7 +313,7 @@ __global__ __launch_bounds__(256, 2) void router_mfma_kernel(const u16* __restri
         const int64_t t = min(t0 + 16 * i + (lane & 15), T - 1);   // rows past the end repeat; not stored
         ap[i] = x + t * d + kb + kq;
     }
-    const int ew = wave * (NTW * 16);
+    const int ew = (blockIdx.z * 4 + wave) * (NTW * 16);     // blockIdx.z: a quarter-block of experts (small T)
     const u16* bp[NTW][3];
 #pragma unroll
     for (int j = 0; j < NTW; ++j)
@@ -463,7 +463,17 @@ void launch_router(const Shape& s, const void* x, const float* Wr, const float* 
             if (s.E == 256) BEAM_RMMA(4, true); else BEAM_RMMA(2, true);
             return;
         }
-        if (s.E == 256) BEAM_RMMA(4, false); else BEAM_RMMA(2, false);
+        if ((int64_t)tb * ks <= 256) {
+            // few token blocks (decode): the experts of a block split over E/64 blocks, one 16-expert
+            // tile per wave, for four times the blocks; each logit is summed in the same order
+            hipLaunchKernelGGL((router_mfma_kernel<1, false>), dim3(tb, (unsigned)ks, (unsigned)(s.E / 64)), dim3(256),
+                               0, st, (const u16*)x, (const u16*)wrs, z_part, s.T, s.d, s.E, s.d / ks, s.G, s.KG, s.K,
+                               s.S, s.norm, bias, idx, w, logits);
+        } else if (s.E == 256) {
+            BEAM_RMMA(4, false);
+        } else {
+            BEAM_RMMA(2, false);
+        }
 #undef BEAM_RMMA
     } else {
         dim3 grid(tb, (unsigned)((s.E + RE - 1) / RE), (unsigned)ks);
