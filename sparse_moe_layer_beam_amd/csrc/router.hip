@@ -244,6 +244,44 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
     select_token<EPL>(z, lane, E, G, KG, K, S, norm, bias, idx + t * K, wout + t * K, logits ? logits + t * E : nullptr);
 }
 
+// The same selection for E = 256 when each logit has many partial sums and the tokens are few
+// (decode): one token per block, the four waves each add a contiguous quarter of the parts
+// (one batch of loads in flight each), then wave 0 adds the four quarter sums in order and
+// selects. Deterministic; the sum is grouped by quarters instead of running left to right.
+__global__ __launch_bounds__(256) void router_topk_quarters_kernel(const float* __restrict__ zp, int ks, int64_t T,
+                                                                   int E, int G, int KG, int K, float S, int norm,
+                                                                   const float* __restrict__ bias,
+                                                                   int32_t* __restrict__ idx, float* __restrict__ wout,
+                                                                   float* __restrict__ logits, int P) {
+    constexpr int kBatch = 16;
+    __shared__ float4 qsum[3][64];
+    const int lane = threadIdx.x & 63, q = threadIdx.x >> 6;
+    const int64_t t = blockIdx.x;
+    const int parts = ks * P, per = (parts + 3) / 4;
+    const int j0 = q * per, j1 = min(parts, j0 + per);
+    auto at = [&](int j) { return zp + ((int64_t)(j / P) * T + t) * (P * E) + (j % P) * E + 4 * lane; };
+    float4 z = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int j = j0; j < j1; j += kBatch) {
+        float4 v[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+            if (j + u < j1) v[u] = *reinterpret_cast<const float4*>(at(j + u));
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+            if (j + u < j1) { z.x += v[u].x; z.y += v[u].y; z.z += v[u].z; z.w += v[u].w; }
+    }
+    if (q > 0) qsum[q - 1][lane] = z;
+    __syncthreads();
+    if (q != 0) return;
+    float zz[4] = {z.x, z.y, z.z, z.w};
+#pragma unroll
+    for (int r = 0; r < 3; ++r) {
+        const float4 o = qsum[r][lane];
+        zz[0] += o.x; zz[1] += o.y; zz[2] += o.z; zz[3] += o.w;
+    }
+    select_token<4>(zz, lane, E, G, KG, K, S, norm, bias, idx + t * K, wout + t * K, logits ? logits + t * E : nullptr);
+}
+
 // ---------------------------------------------------------------------------------------
 // Router GEMM on BF16 MFMA with FP32-exact products. Each FP32 router weight is split into
 // three bf16 parts (hi + mid + lo = w exactly: 8 + 8 + 8 significant bits); x is bf16 already,
@@ -394,6 +432,13 @@ bool router_uses_mfma(const Shape& s) { return (s.E == 128 || s.E == 256) && s.d
 
 // Blocks of 64 tokens; batches of 1024+ blocks run the fused full-K kernel, smaller ones split
 // K so that about 1024 blocks share the work (and the 5 MB router weight).
+#ifndef BEAM_TOPK_QUARTERS_MIN_PARTS
+#define BEAM_TOPK_QUARTERS_MIN_PARTS 16
+#endif
+#ifndef BEAM_TOPK_QUARTERS_MAX_T
+#define BEAM_TOPK_QUARTERS_MAX_T 1024
+#endif
+
 int router_ksplit(const Shape& s) {
     const int64_t tb = (s.T + 63) / 64;
     if (router_uses_mfma(s)) {
@@ -479,6 +524,11 @@ void launch_router(const Shape& s, const void* x, const float* Wr, const float* 
         dim3 grid(tb, (unsigned)((s.E + RE - 1) / RE), (unsigned)ks);
         hipLaunchKernelGGL(router_logits_kernel, grid, dim3(256), 0, st, (const u16*)x, Wr, z_part, s.T, s.d, s.E,
                            s.d / ks);
+    }
+    if (s.E == 256 && ks * P >= BEAM_TOPK_QUARTERS_MIN_PARTS && s.T <= BEAM_TOPK_QUARTERS_MAX_T) {
+        hipLaunchKernelGGL(router_topk_quarters_kernel, dim3((unsigned)s.T), dim3(256), 0, st, z_part, ks, s.T, s.E,
+                           s.G, s.KG, s.K, s.S, s.norm, bias, idx, w, logits, P);
+        return;
     }
     dim3 grid((unsigned)((s.T + 3) / 4));
 #define BEAM_TOPK(N)                                                                                              \
