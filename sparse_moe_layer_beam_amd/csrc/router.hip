@@ -288,6 +288,17 @@ __global__ __launch_bounds__(256) void router_topk_quarters_kernel(const float* 
 // so x*hi, x*mid and x*lo are exact and are accumulated in FP32 by the MFMA, the same FP32
 // dot product the vector path computes, about 10x faster.
 
+// w = hi + mid + lo exactly: hi and mid are w and its first remainder cut to bf16, lo the
+// second remainder rounded to bf16 (bit patterns in the low 16 bits of each output).
+__device__ __forceinline__ void split3(float w, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+    const float h = __uint_as_float(__float_as_uint(w) & 0xffff0000u);
+    const float r1 = w - h;
+    const float m = __uint_as_float(__float_as_uint(r1) & 0xffff0000u);
+    hi = __float_as_uint(h) >> 16;
+    mid = __float_as_uint(m) >> 16;
+    lo = (uint32_t)f32_to_bf16(r1 - m);
+}
+
 // Wr [d, E] fp32 -> WrS [3][E][d] bf16 (expert-major, k contiguous: the MFMA B-operand layout).
 __global__ __launch_bounds__(256) void router_split_kernel(const float* __restrict__ Wr, u16* __restrict__ WrS,
                                                            int d, int E) {
@@ -306,16 +317,7 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float* __restri
         for (int j = 0; j < 8; j += 2) {
             uint32_t h2[3][2];
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                const float w = tile[kc + j + jj][e];
-                const float hi = __uint_as_float(__float_as_uint(w) & 0xffff0000u);
-                const float r1 = w - hi;
-                const float mid = __uint_as_float(__float_as_uint(r1) & 0xffff0000u);
-                const float r2 = r1 - mid;
-                h2[0][jj] = __float_as_uint(hi) >> 16;
-                h2[1][jj] = __float_as_uint(mid) >> 16;
-                h2[2][jj] = (uint32_t)f32_to_bf16(r2);
-            }
+            for (int jj = 0; jj < 2; ++jj) split3(tile[kc + j + jj][e], h2[0][jj], h2[1][jj], h2[2][jj]);
 #pragma unroll
             for (int pl = 0; pl < 3; ++pl) p[pl][j / 2] = h2[pl][0] | (h2[pl][1] << 16);
         }
@@ -333,8 +335,10 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 // Block: 64 tokens x E experts (4 waves of E/4 experts = NTW tiles of 16), k range
 // [blockIdx.y*kc, +kc). FUSED (kc = d): logits go through LDS and the block selects the
 // experts of its 64 tokens. Otherwise the partial logits go to zp[blockIdx.y].
-template <int NTW, bool FUSED>
-__global__ __launch_bounds__(256, 2) void router_mfma_kernel(const u16* __restrict__ x, const u16* __restrict__ WrS,
+// RAW: the weights come as the FP32 Wr [d, E] itself and are split in registers (few tokens:
+// the split copy would cost a launch and more bytes than it saves).
+template <int NTW, bool FUSED, bool RAW = false>
+__global__ __launch_bounds__(256, 2) void router_mfma_kernel(const u16* __restrict__ x, const void* __restrict__ Wsrc,
                                                              float* __restrict__ zp, int64_t T, int d, int E, int kc,
                                                              int G, int KG, int K, float S, int norm,
                                                              const float* __restrict__ bias,
@@ -352,26 +356,55 @@ __global__ __launch_bounds__(256, 2) void router_mfma_kernel(const u16* __restri
         ap[i] = x + t * d + kb + kq;
     }
     const int ew = (blockIdx.z * 4 + wave) * (NTW * 16);     // blockIdx.z: a quarter-block of experts (small T)
+    const u16* const WrS = reinterpret_cast<const u16*>(Wsrc);
+    const float* const Wr = reinterpret_cast<const float*>(Wsrc);
     const u16* bp[NTW][3];
+    const float* fp[NTW];
 #pragma unroll
-    for (int j = 0; j < NTW; ++j)
+    for (int j = 0; j < NTW; ++j) {
+        if constexpr (RAW) fp[j] = Wr + (size_t)(kb + kq) * E + ew + 16 * j + (lane & 15);
+        else
 #pragma unroll
-        for (int pl = 0; pl < 3; ++pl) bp[j][pl] = WrS + ((size_t)pl * E + ew + 16 * j + (lane & 15)) * d + kb + kq;
+            for (int pl = 0; pl < 3; ++pl) bp[j][pl] = WrS + ((size_t)pl * E + ew + 16 * j + (lane & 15)) * d + kb + kq;
+    }
     f32x4 acc[4][NTW];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < NTW; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
     bf16x8 a[2][4], bw[2][NTW][3];
+    float raw[2][NTW][8];
     auto load = [&](int buf, int k) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) a[buf][i] = *reinterpret_cast<const bf16x8*>(ap[i] + k);
 #pragma unroll
-        for (int j = 0; j < NTW; ++j)
+        for (int j = 0; j < NTW; ++j) {
+            if constexpr (RAW) {
 #pragma unroll
-            for (int pl = 0; pl < 3; ++pl) bw[buf][j][pl] = *reinterpret_cast<const bf16x8*>(bp[j][pl] + k);
+                for (int u = 0; u < 8; ++u) raw[buf][j][u] = fp[j][(size_t)(k + u) * E];
+            } else {
+#pragma unroll
+                for (int pl = 0; pl < 3; ++pl) bw[buf][j][pl] = *reinterpret_cast<const bf16x8*>(bp[j][pl] + k);
+            }
+        }
     };
     auto mma = [&](int buf) {
+        if constexpr (RAW) {
+#pragma unroll
+            for (int j = 0; j < NTW; ++j) {
+                u32x4 p[3];
+#pragma unroll
+                for (int u = 0; u < 8; u += 2) {
+                    uint32_t h0[3], h1[3];
+                    split3(raw[buf][j][u], h0[0], h0[1], h0[2]);
+                    split3(raw[buf][j][u + 1], h1[0], h1[1], h1[2]);
+#pragma unroll
+                    for (int pl = 0; pl < 3; ++pl) p[pl][u / 2] = h0[pl] | (h1[pl] << 16);
+                }
+#pragma unroll
+                for (int pl = 0; pl < 3; ++pl) bw[buf][j][pl] = __builtin_bit_cast(bf16x8, p[pl]);
+            }
+        }
 #pragma unroll
         for (int pl = 0; pl < 3; ++pl)
 #pragma unroll
@@ -432,6 +465,9 @@ bool router_uses_mfma(const Shape& s) { return (s.E == 128 || s.E == 256) && s.d
 
 // Blocks of 64 tokens; batches of 1024+ blocks run the fused full-K kernel, smaller ones split
 // K so that about 1024 blocks share the work (and the 5 MB router weight).
+#ifndef BEAM_ROUTER_RAW_SMALL
+#define BEAM_ROUTER_RAW_SMALL 1
+#endif
 #ifndef BEAM_TOPK_QUARTERS_MIN_PARTS
 #define BEAM_TOPK_QUARTERS_MIN_PARTS 16
 #endif
@@ -498,8 +534,10 @@ void launch_router(const Shape& s, const void* x, const float* Wr, const float* 
                            Wr, (u16*)wrs, s.d, s.E);
         launch_gemm_router(s, x, wrs, z_part, gks, st);
     } else if (router_uses_mfma(s)) {
-        hipLaunchKernelGGL(router_split_kernel, dim3((unsigned)(s.d / 64), (unsigned)(s.E / 64)), dim3(256), 0, st,
-                           Wr, (u16*)wrs, s.d, s.E);
+        const bool small = (int64_t)tb * ks <= 256 && ks > 1;
+        if (!small)
+            hipLaunchKernelGGL(router_split_kernel, dim3((unsigned)(s.d / 64), (unsigned)(s.E / 64)), dim3(256), 0,
+                               st, Wr, (u16*)wrs, s.d, s.E);
 #define BEAM_RMMA(NTW, F)                                                                                        \
     hipLaunchKernelGGL((router_mfma_kernel<NTW, F>), dim3(tb, (unsigned)ks), dim3(256), 0, st, (const u16*)x,     \
                        (const u16*)wrs, z_part, s.T, s.d, s.E, s.d / ks, s.G, s.KG, s.K, s.S, s.norm, bias, idx, w, \
@@ -508,12 +546,20 @@ void launch_router(const Shape& s, const void* x, const float* Wr, const float* 
             if (s.E == 256) BEAM_RMMA(4, true); else BEAM_RMMA(2, true);
             return;
         }
-        if ((int64_t)tb * ks <= 256) {
+        if (small) {
             // few token blocks (decode): the experts of a block split over E/64 blocks, one 16-expert
             // tile per wave, for four times the blocks; each logit is summed in the same order
+#if BEAM_ROUTER_RAW_SMALL
+            hipLaunchKernelGGL((router_mfma_kernel<1, false, true>), dim3(tb, (unsigned)ks, (unsigned)(s.E / 64)),
+                               dim3(256), 0, st, (const u16*)x, (const void*)Wr, z_part, s.T, s.d, s.E, s.d / ks, s.G,
+                               s.KG, s.K, s.S, s.norm, bias, idx, w, logits);
+#else
+            hipLaunchKernelGGL(router_split_kernel, dim3((unsigned)(s.d / 64), (unsigned)(s.E / 64)), dim3(256), 0, st,
+                               Wr, (u16*)wrs, s.d, s.E);
             hipLaunchKernelGGL((router_mfma_kernel<1, false>), dim3(tb, (unsigned)ks, (unsigned)(s.E / 64)), dim3(256),
                                0, st, (const u16*)x, (const u16*)wrs, z_part, s.T, s.d, s.E, s.d / ks, s.G, s.KG, s.K,
                                s.S, s.norm, bias, idx, w, logits);
+#endif
         } else if (s.E == 256) {
             BEAM_RMMA(4, false);
         } else {
