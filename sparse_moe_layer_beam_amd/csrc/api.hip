@@ -211,8 +211,10 @@ beam_moe_status forward_impl(const beam_moe_shape* shape, const void* x, const v
     int32_t* pr = at<int32_t>(workspace, L.pr);
     int32_t* tiles = at<int32_t>(workspace, L.tiles);
     int32_t* ntiles = at<int32_t>(workspace, L.ntiles);
-    beam::launch_dispatch(s, idx, off, sp, pr, at<int32_t>(workspace, L.cc), at<int32_t>(workspace, L.ric), tiles,
-                          ntiles, beam::experts_tile_m(s), hs);
+    // the tile list feeds only the tiled GEMMs; the weight streams read the offsets alone
+    const bool tiled = !fp8 && beam::experts_tiled(s);
+    beam::launch_dispatch(s, idx, off, sp, pr, at<int32_t>(workspace, L.cc), at<int32_t>(workspace, L.ric),
+                          tiled ? tiles : nullptr, ntiles, beam::experts_tile_m(s), hs);
     mark(2);
     void* h = at<void>(workspace, L.h);
     float* yp = at<float>(workspace, L.yp);
@@ -383,8 +385,8 @@ beam_moe_status beam_moe_experts_share(const beam_moe_shape* shape, int32_t e_be
     mark(0);
     mark(1);
     beam::launch_share_idx(topk_idx, s.T * s.K, e_begin, e_count, idl, hs);
-    beam::launch_dispatch(sl, idl, off, sp, pr, at<int32_t>(workspace, L.cc), at<int32_t>(workspace, L.ric), tiles,
-                          ntiles, beam::experts_tile_m(sl), hs);
+    beam::launch_dispatch(sl, idl, off, sp, pr, at<int32_t>(workspace, L.cc), at<int32_t>(workspace, L.ric),
+                          beam::experts_tiled(sl) ? tiles : nullptr, ntiles, beam::experts_tile_m(sl), hs);
     mark(2);
     beam::launch_swiglu(sl, x, off, sp, tiles, ntiles, Wg, Wu, h, hs);
     mark(3);
