@@ -47,6 +47,9 @@ SMALL = {
     # half past the end
     "mid_T2100": Workload(35, "mid_T2100", T=2100, **_MID),
     "e128_T2100": Workload(36, "e128_T2100", T=2100, d=256, E=128, n_group=4, topk_group=2, top_k=6, I=128),
+    # d = 2048 below T = 1024: 16 k parts per logit, so the top-k adds them a quarter per wave, and
+    # 16 token blocks x 16 parts still take the router path that splits the FP32 weight in registers
+    "d2048_T1000": Workload(37, "d2048_T1000", T=1000, d=2048, E=256, n_group=8, topk_group=4, top_k=8, I=128),
 }
 BEAM = {i: recipes.WORKLOADS[i] for i in (1, 2, 3, 4)}
 
