@@ -77,6 +77,52 @@ def output_error(y_gpu, y_ref):
     return err, rms
 
 
+def segment_blocks(idx_ref, E, block):
+    """(expert, block) of every pair, in the expert-major stable order the dispatch defines:
+    pair p = t*K + j sits at rank r inside its expert's segment and in block r // block.
+    Returns (token of each pair, key of each pair, rank of each pair)."""
+    flat = np.asarray(idx_ref, np.int64).reshape(-1)
+    K = idx_ref.shape[1]
+    order = np.argsort(flat, kind="stable")
+    counts = np.bincount(flat, minlength=E)
+    starts = np.concatenate([[0], np.cumsum(counts)[:-1]])
+    rank = np.empty_like(order)
+    rank[order] = np.arange(len(order)) - starts[flat[order]]
+    key = flat * (1 << 20) + rank // block
+    return np.arange(len(flat)) // K, key, rank
+
+
+def cover_tokens(idx_ref, E, block, tails=True):
+    """Tokens such that every (expert, block of `block` consecutive rows of its segment) holds
+    at least one of them, plus (tails) the token of each expert's last row: every work item of
+    a grouped GEMM whose m-tiles are multiples of `block` rows then computes at least one
+    compared output row, the ragged last tile of every expert included. Greedy set cover: each
+    token covers the K blocks of its K pairs."""
+    tok, key, rank = segment_blocks(idx_ref, E, block)
+    K = idx_ref.shape[1]
+    picks = set()
+    if tails:
+        flat = np.asarray(idx_ref, np.int64).reshape(-1)
+        counts = np.bincount(flat, minlength=E)
+        last = np.nonzero(rank == counts[flat] - 1)[0]
+        picks.update(int(t) for t in tok[last])
+    covered = set()
+    for t in picks:
+        covered.update(int(k) for k in key[t * K:(t + 1) * K])
+    # for each uncovered block (in key order) take its token that covers the most uncovered blocks
+    members = {}
+    for p, k in enumerate(key.tolist()):
+        members.setdefault(k, []).append(int(tok[p]))
+    for k in sorted(members):
+        if k in covered:
+            continue
+        best = max(members[k], key=lambda t: sum(int(q) not in covered for q in key[t * K:(t + 1) * K]))
+        picks.add(best)
+        covered.update(int(q) for q in key[best * K:(best + 1) * K])
+    assert covered == set(members)
+    return np.array(sorted(picks), dtype=np.int64)
+
+
 def sample_tokens(idx_ref, n_extra=6, seed=0, must=()):
     """Deterministic token sample: first, last, tokens of the busiest expert, random others."""
     T = idx_ref.shape[0]

@@ -186,6 +186,58 @@ def test_route_invariants():
     np.testing.assert_allclose(oracle.weights_for(z, idx, S), wt, rtol=1e-15)
 
 
+def _brute_margins(z_row, bias, G, KG, K):
+    """Both selection margins by exhaustive enumeration, written from their meaning: how much
+    the best admissible choice beats the runner-up. Group stage: every pair of a group gives
+    the group score; the best KG-subset of groups by total score minus the best other
+    KG-subset. Expert stage (inside the best groups): the best K-subset of candidates by
+    total biased score minus the best other K-subset. inf where there is no runner-up."""
+    E = len(z_row)
+    gsz = E // G
+    b = _ref.sigmoid(np.asarray(z_row, np.float64)) + np.asarray(bias, np.float64)
+    gs = [max(b[i] + b[j] for i, j in itertools.combinations(range(g * gsz, (g + 1) * gsz), 2)) for g in range(G)]
+    subsets = sorted((sum(gs[g] for g in c), c) for c in itertools.combinations(range(G), KG))
+    m_group = subsets[-1][0] - subsets[-2][0] if len(subsets) > 1 else math.inf
+    kept = subsets[-1][1]
+    cand = [e for g in kept for e in range(g * gsz, (g + 1) * gsz)]
+    sums = sorted(sum(b[e] for e in c) for c in itertools.combinations(cand, K))
+    m_expert = sums[-1] - sums[-2] if len(sums) > 1 else math.inf
+    return m_group, m_expert
+
+
+def test_route_gap_equals_brute_force_margins():
+    """The oracle's gap (the smaller of the two selection margins, which decides which tokens
+    the GPU parity rule may excuse) against both margins found by enumerating every group
+    subset and every expert subset, on the tiny shape and on random small shapes. A slip in
+    which ranked score the gap subtracts (KG-2 for KG-1, K for K-1, the candidate list before
+    or after the kept-group filter) changes it on most tokens."""
+    cases = []
+    w = recipes.WORKLOADS[0]
+    for shift in (0, 1):
+        _, x, Wr, b = _tiny_inputs(w, shift)
+        cases.append((x, Wr, b, w.n_group, w.topk_group, w.top_k))
+    rng = np.random.default_rng(7)
+    for (E, G, KG, K) in [(8, 2, 1, 2), (12, 3, 2, 3), (16, 4, 3, 5), (16, 8, 3, 4), (20, 5, 4, 6), (16, 4, 4, 3),
+                          (12, 4, 2, 6)]:
+        x = _ref.f64_to_bf16_bits_rne(rng.standard_normal((30, 64)))
+        Wr = (rng.standard_normal((64, E)) / 8).astype(np.float32)
+        bias = rng.uniform(-0.3, 0.3, E).astype(np.float32)
+        cases.append((x, Wr, bias, G, KG, K))
+    n = 0
+    for x, Wr, bias, G, KG, K in cases:
+        _, _, gap = oracle.route(x, Wr, bias, G, KG, K, 2.5)
+        zr = _ref.bf16_bits_to_f64(x) @ Wr.astype(np.float64)
+        for t in range(x.shape[0]):
+            mg, me = _brute_margins(zr[t], bias, G, KG, K)
+            want = min(mg, me)
+            if math.isinf(want):
+                assert math.isinf(gap[t]), (G, KG, K, t)
+            else:
+                assert abs(gap[t] - want) <= 1e-12, (G, KG, K, t, gap[t], mg, me)
+            n += 1
+    assert n == 2 * 128 + 7 * 30
+
+
 def test_route_ties_go_to_lower_index():
     E, G, KG, K, d = 16, 4, 2, 4, 64
     x = np.zeros((1, d), dtype=np.uint16)          # all logits 0, all scores 0.5
