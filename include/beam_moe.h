@@ -205,7 +205,10 @@ beam_moe_status beam_moe_forward_fp8(const beam_moe_shape* shape, const void* x,
  *   y = Wd . bf16(silu(Wg . x) * (Wu . x))   per token, BF16 MFMA with FP32 accumulation,
  * h rounded to bf16 once as in the experts; no routing, no scaling.
  *   T, d, I    tokens, hidden size (5120), intermediate size (20480); d and I multiples of
- *              128, T*d, T*I and d*I below 2^31, else BEAM_MOE_ERR_UNSUPPORTED_SHAPE. T <= 64
+ *              128, I >= 2048, T*d, T*I and d*I below 2^31, else BEAM_MOE_ERR_UNSUPPORTED_SHAPE.
+ *              (h is rounded to bf16 from FP32 sums; where the FP64 sum rounds to the other
+ *              neighbour, one ulp of a large h moves y by about 2^-4 * 3.5 / sqrt(I), which
+ *              reaches 1e-2 * rms(y) near I = 512 and stays near half of it from I = 2048.) T <= 64
  *              (decode): weight streams against the tokens, the reduction over k split in parts
  *              added in a fixed order. Larger T: the tiled GEMM.
  *   weight_layout  BEAM_MOE_WEIGHTS_ROW_MAJOR, or PACKED (Wg, Wu through beam_moe_pack_weights

@@ -309,6 +309,8 @@ beam_moe_status beam_moe_forward_fp8(const beam_moe_shape* shape, const void* x,
                         ws_bytes, stream, stage_events, nullptr, &f);
 }
 
+constexpr int32_t kDenseMinI = 2048;
+
 size_t beam_moe_dense_workspace_bytes(int64_t T, int32_t d, int32_t I) {
     if (T < 0 || d <= 0 || I <= 0) return 0;
     size_t n = up((size_t)T * (size_t)I * 2);
@@ -326,6 +328,10 @@ beam_moe_status beam_moe_dense_mlp(int64_t T, int32_t d, int32_t I, int32_t weig
     if (!aligned(x) || !aligned(Wg) || !aligned(Wu) || !aligned(Wd) || !aligned(y)) return BEAM_MOE_ERR_INVALID_ARG;
     const int64_t lim = (int64_t)1 << 31;
     if (T * (int64_t)d >= lim || T * (int64_t)I >= lim || (int64_t)d * I >= lim) return BEAM_MOE_ERR_UNSUPPORTED_SHAPE;
+    // the output bar (max|dy| <= 1e-2 rms(y)) holds only from I = 2048: one bf16 ulp of one large h
+    // element, rounded from FP32 rather than FP64 sums, moves y by ~2^-4 * 3.5 / sqrt(I) ~ 1e-2 rms(y)
+    // at I = 512
+    if (I < kDenseMinI) return BEAM_MOE_ERR_UNSUPPORTED_SHAPE;
     const bool stream_path = beam::dense_stream_supports(T, d, I);
     if (!stream_path && !beam::dense_supports(T, d, I)) return BEAM_MOE_ERR_UNSUPPORTED_SHAPE;
     if (T == 0) return BEAM_MOE_OK;

@@ -28,35 +28,23 @@
 namespace beam {
 namespace {
 
-#ifndef BEAM_GU_DEPTH
-#define BEAM_GU_DEPTH 6         // gate/up: k-steps of 32 prefetched ahead of the MFMAs
-#endif
-#ifndef BEAM_DN_DEPTH
-#define BEAM_DN_DEPTH 6         // down: the same
-#endif
-#ifndef BEAM_GU_OCC
-#define BEAM_GU_OCC 3           // gate/up: blocks of 4 waves per CU the registers must allow
-#endif
-#ifndef BEAM_DN_OCC
-#define BEAM_DN_OCC 3           // down: the same
-#endif
-#ifndef BEAM_STREAM_MT
-#define BEAM_STREAM_MT 1        // 16-token tiles per pass over an expert's weights
-#endif
-#ifndef BEAM_GU_KSPLIT
-#define BEAM_GU_KSPLIT 4        // gate/up: waves sharing one 16-channel group, each a part of k
-#endif
-#ifndef BEAM_DN_KSPLIT
-#define BEAM_DN_KSPLIT 2        // down: the same
-#endif
+// Tuning of the weight streams, chosen by measurement on MI355X (the sweeps are summarized beside
+// each kernel below).
+constexpr int kGuDepth = 6;             // gate/up: k-steps of 32 prefetched ahead of the MFMAs
+constexpr int kDnDepth = 6;             // down: the same
+constexpr int kGuOcc = 3;               // gate/up: blocks of 4 waves per CU the registers must allow
+constexpr int kDnOcc = 3;               // down: the same
+constexpr int kStreamMT = 1;            // 16-token tiles per pass over an expert's weights
+constexpr int kGuKsplit = 4;            // gate/up: waves sharing one 16-channel group, each a part of k
+constexpr int kDnKsplit = 2;            // down: the same
 
 constexpr int kWavesPerBlock = 4;
 // a block's waves cover whole k-split groups
-static_assert(BEAM_GU_KSPLIT >= 1 && kWavesPerBlock % BEAM_GU_KSPLIT == 0, "gate/up k split must divide 4 waves");
-static_assert(BEAM_DN_KSPLIT >= 1 && kWavesPerBlock % BEAM_DN_KSPLIT == 0, "down k split must divide 4 waves");
-constexpr int kDgu = BEAM_GU_DEPTH;
-constexpr int kDdn = BEAM_DN_DEPTH;
-constexpr int kMT = BEAM_STREAM_MT;
+static_assert(kGuKsplit >= 1 && kWavesPerBlock % kGuKsplit == 0, "gate/up k split must divide 4 waves");
+static_assert(kDnKsplit >= 1 && kWavesPerBlock % kDnKsplit == 0, "down k split must divide 4 waves");
+constexpr int kDgu = kGuDepth;
+constexpr int kDdn = kDnDepth;
+constexpr int kMT = kStreamMT;
 // Weight elements per unit of k: 1 row-major, 16 packed (a 32-k step of a 16-row block is 512
 // contiguous elements).
 template <bool PK>
@@ -167,7 +155,7 @@ __device__ __forceinline__ void ksplit_reduce(f32x4 (&part)[kWavesPerBlock][NA][
 // for down, 1.5% faster than one part and depth 6 at four waves; an 8-deep gate/up ring
 // at three waves per SIMD ran 6% slower.
 template <int KS, bool PK>
-__global__ __launch_bounds__(256, BEAM_GU_OCC) void swiglu_stream_kernel(const u16* __restrict__ x,
+__global__ __launch_bounds__(256, kGuOcc) void swiglu_stream_kernel(const u16* __restrict__ x,
                                                             const int32_t* __restrict__ offsets,
                                                             const int32_t* __restrict__ sorted_pairs, int K,
                                                             const u16* __restrict__ Wg, const u16* __restrict__ Wu,
@@ -226,7 +214,7 @@ __global__ __launch_bounds__(256, BEAM_GU_OCC) void swiglu_stream_kernel(const u
 // grid: (ceil(d / (16 * 4 / KS)), E); block: 4 waves; the KS waves of a 16-row group of Wd
 // each stream a 1/KS part of k, as in the gate/up kernel.
 template <int KS, bool PK>
-__global__ __launch_bounds__(256, BEAM_DN_OCC) void down_stream_kernel(const u16* __restrict__ h,
+__global__ __launch_bounds__(256, kDnOcc) void down_stream_kernel(const u16* __restrict__ h,
                                                           const int32_t* __restrict__ offsets,
                                                           const int32_t* __restrict__ sorted_pairs,
                                                           const float* __restrict__ topk_w,
@@ -472,14 +460,14 @@ void launch_swiglu(const Shape& s, const void* x, const int32_t* offsets, const 
         return;
     }
     // k parts must be whole 32-wide MFMA steps
-    const int ks = s.d % (32 * BEAM_GU_KSPLIT) == 0 ? BEAM_GU_KSPLIT : 1;
+    const int ks = s.d % (32 * kGuKsplit) == 0 ? kGuKsplit : 1;
     const int per_block = kWavesPerBlock / ks * 16;
     const dim3 grid((unsigned)((s.I + per_block - 1) / per_block), (unsigned)s.E);
 #define BEAM_GU(KS, PK)                                                                                       \
     hipLaunchKernelGGL((swiglu_stream_kernel<KS, PK>), grid, dim3(256), 0, st, (const u16*)x, offsets,         \
                        sorted_pairs, s.K, (const u16*)Wg, (const u16*)Wu, (u16*)h, s.d, s.I)
-    if (ks == BEAM_GU_KSPLIT) {
-        if (s.packed) BEAM_GU(BEAM_GU_KSPLIT, true); else BEAM_GU(BEAM_GU_KSPLIT, false);
+    if (ks == kGuKsplit) {
+        if (s.packed) BEAM_GU(kGuKsplit, true); else BEAM_GU(kGuKsplit, false);
     } else {
         if (s.packed) BEAM_GU(1, true); else BEAM_GU(1, false);
     }
@@ -493,14 +481,14 @@ void launch_down(const Shape& s, const void* h, const int32_t* offsets, const in
         launch_gemm_down(s, h, offsets, sorted_pairs, topk_w, tiles, n_tiles, Wd, y_perm, st);
         return;
     }
-    const int ks = s.I % (32 * BEAM_DN_KSPLIT) == 0 ? BEAM_DN_KSPLIT : 1;
+    const int ks = s.I % (32 * kDnKsplit) == 0 ? kDnKsplit : 1;
     const int per_block = kWavesPerBlock / ks * 16;
     const dim3 grid((unsigned)((s.d + per_block - 1) / per_block), (unsigned)s.E);
 #define BEAM_DN(KS, PK)                                                                                       \
     hipLaunchKernelGGL((down_stream_kernel<KS, PK>), grid, dim3(256), 0, st, (const u16*)h, offsets,           \
                        sorted_pairs, topk_w, (const u16*)Wd, y_perm, s.d, s.I)
-    if (ks == BEAM_DN_KSPLIT) {
-        if (s.packed) BEAM_DN(BEAM_DN_KSPLIT, true); else BEAM_DN(BEAM_DN_KSPLIT, false);
+    if (ks == kDnKsplit) {
+        if (s.packed) BEAM_DN(kDnKsplit, true); else BEAM_DN(kDnKsplit, false);
     } else {
         if (s.packed) BEAM_DN(1, true); else BEAM_DN(1, false);
     }

@@ -22,10 +22,7 @@ namespace {
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;
-#ifndef BEAM_FP8_D
-#define BEAM_FP8_D 8
-#endif
-constexpr int kD = BEAM_FP8_D;   // 64-k steps in flight per wave (8: one group of scale bytes)
+constexpr int kD = 8;   // 64-k steps in flight per wave (8: one group of scale bytes)
 
 // ---- quantization --------------------------------------------------------------------------
 
@@ -216,10 +213,7 @@ __global__ __launch_bounds__(256) void swiglu_fp8_kernel(const u16* __restrict__
 // y_perm[beg+m, n] = w_pair * (h[beg+m] . Wd[e,n]) with fp8 Wd. grid: (ceil(d / (64 * kDnRB)), E);
 // block: 4 waves, each streaming kDnRB blocks of 16 output channels whose rows share the
 // activation fragments (one 16-row block of 1-byte codes is only a 40 KB stream at I = 2560).
-#ifndef BEAM_FP8_DN_RB
-#define BEAM_FP8_DN_RB 2
-#endif
-constexpr int kDnRB = BEAM_FP8_DN_RB;
+constexpr int kDnRB = 2;
 template <bool PK>
 __global__ __launch_bounds__(256) void down_fp8_kernel(const u16* __restrict__ h, const int32_t* __restrict__ offsets,
                                                        const int32_t* __restrict__ sorted_pairs,

@@ -463,17 +463,13 @@ void launch_rmsnorm(const Shape& s, const void* h, const void* w, void* x_out, h
 
 bool router_uses_mfma(const Shape& s) { return (s.E == 128 || s.E == 256) && s.d % 64 == 0; }
 
+// The quarter-split selection (router_topk_quarters_kernel) takes E = 256 batches of at most
+// this many tokens whose logits have at least this many partial sums.
+constexpr int kQuartersMinParts = 16;
+constexpr int64_t kQuartersMaxT = 1024;
+
 // Blocks of 64 tokens; batches of 1024+ blocks run the fused full-K kernel, smaller ones split
 // K so that about 1024 blocks share the work (and the 5 MB router weight).
-#ifndef BEAM_ROUTER_RAW_SMALL
-#define BEAM_ROUTER_RAW_SMALL 1
-#endif
-#ifndef BEAM_TOPK_QUARTERS_MIN_PARTS
-#define BEAM_TOPK_QUARTERS_MIN_PARTS 16
-#endif
-#ifndef BEAM_TOPK_QUARTERS_MAX_T
-#define BEAM_TOPK_QUARTERS_MAX_T 1024
-#endif
 
 int router_ksplit(const Shape& s) {
     const int64_t tb = (s.T + 63) / 64;
@@ -503,16 +499,12 @@ size_t router_split_bytes(const Shape& s) { return router_uses_mfma(s) ? (size_t
 // 256 tiles): the 64-token blocks of router_mfma_kernel each reload all 3E rows of the split
 // weight in MFMA operand layout, which bounds them by the L2-to-CU load rate. k is cut into the
 // fewest parts (of 1, 2, 4, 8) that give at least two items per CU. 0: not this route.
-#ifndef BEAM_ROUTER_GEMM_MIN_T
-#define BEAM_ROUTER_GEMM_MIN_T 2048
-#endif
-#ifndef BEAM_ROUTER_GEMM_ITEMS
-#define BEAM_ROUTER_GEMM_ITEMS 512
-#endif
+constexpr int64_t kRouterGemmMinT = 2048;
+constexpr int kRouterGemmItems = 512;
 int router_gemm_ks(const Shape& s) {
-    if (!router_uses_mfma(s) || s.T < BEAM_ROUTER_GEMM_MIN_T || s.d % 128 != 0) return 0;
+    if (!router_uses_mfma(s) || s.T < kRouterGemmMinT || s.d % 128 != 0) return 0;
     int ks = 1;
-    while (ks < 8 && gemm_router_items(s, ks) < BEAM_ROUTER_GEMM_ITEMS && s.d % (64 * 2 * ks) == 0) ks *= 2;
+    while (ks < 8 && gemm_router_items(s, ks) < kRouterGemmItems && s.d % (64 * 2 * ks) == 0) ks *= 2;
     return ks;
 }
 
@@ -549,17 +541,9 @@ void launch_router(const Shape& s, const void* x, const float* Wr, const float* 
         if (small) {
             // few token blocks (decode): the experts of a block split over E/64 blocks, one 16-expert
             // tile per wave, for four times the blocks; each logit is summed in the same order
-#if BEAM_ROUTER_RAW_SMALL
             hipLaunchKernelGGL((router_mfma_kernel<1, false, true>), dim3(tb, (unsigned)ks, (unsigned)(s.E / 64)),
                                dim3(256), 0, st, (const u16*)x, (const void*)Wr, z_part, s.T, s.d, s.E, s.d / ks, s.G,
                                s.KG, s.K, s.S, s.norm, bias, idx, w, logits);
-#else
-            hipLaunchKernelGGL(router_split_kernel, dim3((unsigned)(s.d / 64), (unsigned)(s.E / 64)), dim3(256), 0, st,
-                               Wr, (u16*)wrs, s.d, s.E);
-            hipLaunchKernelGGL((router_mfma_kernel<1, false>), dim3(tb, (unsigned)ks, (unsigned)(s.E / 64)), dim3(256),
-                               0, st, (const u16*)x, (const u16*)wrs, z_part, s.T, s.d, s.E, s.d / ks, s.G, s.KG, s.K,
-                               s.S, s.norm, bias, idx, w, logits);
-#endif
         } else if (s.E == 256) {
             BEAM_RMMA(4, false);
         } else {
@@ -571,7 +555,7 @@ void launch_router(const Shape& s, const void* x, const float* Wr, const float* 
         hipLaunchKernelGGL(router_logits_kernel, grid, dim3(256), 0, st, (const u16*)x, Wr, z_part, s.T, s.d, s.E,
                            s.d / ks);
     }
-    if (s.E == 256 && ks * P >= BEAM_TOPK_QUARTERS_MIN_PARTS && s.T <= BEAM_TOPK_QUARTERS_MAX_T) {
+    if (s.E == 256 && ks * P >= kQuartersMinParts && s.T <= kQuartersMaxT) {
         hipLaunchKernelGGL(router_topk_quarters_kernel, dim3((unsigned)s.T), dim3(256), 0, st, z_part, ks, s.T, s.E,
                            s.G, s.KG, s.K, s.S, s.norm, bias, idx, w, logits, P);
         return;

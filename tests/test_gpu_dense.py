@@ -70,3 +70,19 @@ def test_dense_beam_shape_sampled(cfg):
     print("%s: %d sampled tokens, max|dy| %.3e, rms %.3e" % (w.name, len(rows), err, rms))
     assert np.isfinite(y).all()
     assert err <= P.Y_TOL * rms
+
+
+def test_dense_smallest_intermediate_every_token():
+    """The smallest accepted intermediate size (I = 2048) at d = 2048 and T = 2000, every token:
+    where the bf16 rounding of h from FP32 sums weighs most against the output bar (at I = 512 a
+    single one-ulp difference of a large h reaches about 1e-2 rms(y), which is why the entry point
+    rejects I < 2048)."""
+    w = recipes.DenseWorkload(13, "dense_d2048_I2048_T2000", T=2000, d=2048, I=2048)
+    print("case", w.name, flush=True)
+    t = synth.dense_device_inputs(w)
+    y = _run(w, t)
+    ref = oracle.expert(synth.dense_hidden(w), *synth.dense_weights(w))
+    err, rms = P.output_error(y, ref)
+    print("%s: max|dy| %.3e, rms %.3e, ratio %.2e" % (w.name, err, rms, err / rms))
+    assert np.isfinite(y).all()
+    assert err <= P.Y_TOL * rms

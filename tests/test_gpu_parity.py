@@ -50,6 +50,9 @@ SMALL = {
     # d = 2048 below T = 1024: 16 k parts per logit, so the top-k adds them a quarter per wave, and
     # 16 token blocks x 16 parts still take the router path that splits the FP32 weight in registers
     "d2048_T1000": Workload(37, "d2048_T1000", T=1000, d=2048, E=256, n_group=8, topk_group=4, top_k=8, I=128),
+    # d = 2304 at T = 64: k in 18 parts, so the quarter-split top-k adds uneven quarters (5, 5, 5, 3)
+    # and the in-register router weight split runs at 18 parts
+    "d2304_T64": Workload(38, "d2304_T64", T=64, d=2304, E=256, n_group=8, topk_group=4, top_k=8, I=128),
 }
 BEAM = {i: recipes.WORKLOADS[i] for i in (1, 2, 3, 4)}
 
