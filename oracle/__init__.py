@@ -62,8 +62,21 @@ def lib():
     return _lib
 
 
+_THREADS = None
+
+
 def nthreads() -> int:
+    """Threads of the oracle's parallel loops: the host's cores, at most 16 (the CPU share of one
+    GPU on the boxes this runs on), unless set_threads() fixed a number."""
+    if _THREADS is not None:
+        return _THREADS
     return max(1, min(16, os.cpu_count() or 1))
+
+
+def set_threads(n) -> None:
+    """Fix the oracle's thread count (None: back to the default)."""
+    global _THREADS
+    _THREADS = None if n is None else max(1, int(n))
 
 
 def _c(a, dtype):
