@@ -263,6 +263,21 @@ beam_moe_status beam_moe_experts_share(const beam_moe_shape* shape, int32_t e_be
  * Pointers 16-byte aligned; rows * K below 2^40. rows = 0 returns BEAM_MOE_OK. */
 beam_moe_status beam_moe_pack_weights(int64_t rows, int32_t K, const void* w, void* packed, void* stream);
 
+/* beam_moe_forward without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same validation, kernels and results (bitwise) as beam_moe_forward, with its workspace
+ * taken from a fixed 64 MiB scratch array that the library holds on each GPU it runs on until
+ * the process ends (enough for the Beam shape up to T = 192 tokens). The call allocates and
+ * frees nothing. A shape whose beam_moe_workspace_bytes exceeds 64 MiB returns
+ * BEAM_MOE_ERR_WORKSPACE_TOO_SMALL before any GPU work. Every call on one GPU shares that GPU's
+ * scratch, which keeps the last call's contents (nothing in it has to start at zero): calls that
+ * overlap on one GPU (on different streams, or from several threads) race, and the caller must
+ * order them. */
+beam_moe_status beam_moe_forward_noalloc(const beam_moe_shape* shape, const void* x, const void* norm_w,
+                                         const float* Wr, const float* bias, const void* Wg, const void* Wu,
+                                         const void* Wd, float* y, int32_t* topk_idx, float* topk_w, float* logits,
+                                         void* stream);
+
 /* Static, human-readable name of a status code; "unknown status" for any other value (the
  * argument is a plain int so that any value a caller passes is well defined). */
 const char* beam_moe_status_string(int32_t status);

@@ -24,7 +24,7 @@ EXPORTED = ("beam_moe_workspace_bytes", "beam_moe_route", "beam_moe_dispatch", "
             "beam_moe_forward_staged", "beam_moe_post_residual", "beam_moe_forward_residual",
             "beam_moe_dense_workspace_bytes", "beam_moe_dense_mlp", "beam_moe_quantize_fp8",
             "beam_moe_forward_fp8", "beam_moe_share_workspace_bytes", "beam_moe_experts_share",
-            "beam_moe_pack_weights", "beam_moe_status_string")
+            "beam_moe_pack_weights", "beam_moe_forward_noalloc", "beam_moe_status_string")
 N_STAGE_EVENTS = 6
 
 
@@ -92,6 +92,8 @@ def lib() -> ctypes.CDLL:
         L.beam_moe_experts_share.restype = i32
         L.beam_moe_pack_weights.argtypes = [ctypes.c_int64, i32, vp, vp, vp]
         L.beam_moe_pack_weights.restype = i32
+        L.beam_moe_forward_noalloc.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.beam_moe_forward_noalloc.restype = i32
         L.beam_moe_status_string.argtypes = [i32]
         L.beam_moe_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -164,6 +166,15 @@ def beam_moe_forward(shape, x, norm_w, Wr, bias, Wg, Wu, Wd, y, topk_idx, topk_w
                                 _ptr(Wu), _ptr(Wd), _ptr(y), _ptr(topk_idx), _ptr(topk_w), _ptr(logits),
                                 _ptr(workspace), _nbytes(workspace), _stream(stream))
     return _check(st, "beam_moe_forward") if check else st
+
+
+def beam_moe_forward_noalloc(shape, x, norm_w, Wr, bias, Wg, Wu, Wd, y, topk_idx, topk_w, logits, stream=None,
+                             check=True) -> int:
+    """beam_moe_forward on the library's fixed per-GPU scratch (no workspace argument, no allocation)."""
+    st = lib().beam_moe_forward_noalloc(ctypes.byref(shape), _ptr(x), _ptr(norm_w), _ptr(Wr), _ptr(bias), _ptr(Wg),
+                                        _ptr(Wu), _ptr(Wd), _ptr(y), _ptr(topk_idx), _ptr(topk_w), _ptr(logits),
+                                        _stream(stream))
+    return _check(st, "beam_moe_forward_noalloc") if check else st
 
 
 def beam_moe_forward_staged(shape, x, norm_w, Wr, bias, Wg, Wu, Wd, y, topk_idx, topk_w, logits, workspace,

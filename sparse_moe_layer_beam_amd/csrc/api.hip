@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/beam_moe.h"
 #include "kernels.h"
@@ -171,6 +172,19 @@ beam_moe_status check_post(const Shape& s, const Post& p) {
     return BEAM_MOE_OK;
 }
 
+// The layer's tensor arguments: required ones present, all 16-byte aligned (y may be absent when
+// the post-MLP residual takes the output).
+beam_moe_status check_tensors(const void* x, const void* norm_w, const float* Wr, const float* bias, const void* Wg,
+                              const void* Wu, const void* Wd, const float* y, const int32_t* topk_idx,
+                              const float* topk_w, const float* logits, bool post) {
+    if (!x || !Wr || !bias || !Wg || !Wu || !Wd || (!y && !post)) return BEAM_MOE_ERR_INVALID_ARG;
+    if (!aligned(x) || !aligned(Wr) || !aligned(bias) || !aligned(Wg) || !aligned(Wu) || !aligned(Wd) ||
+        (y && !aligned(y)) || (norm_w && !aligned(norm_w)) || (topk_idx && !aligned(topk_idx)) ||
+        (topk_w && !aligned(topk_w)) || (logits && !aligned(logits)))
+        return BEAM_MOE_ERR_INVALID_ARG;
+    return BEAM_MOE_OK;
+}
+
 beam_moe_status forward_impl(const beam_moe_shape* shape, const void* x, const void* norm_w, const float* Wr,
                              const float* bias, const void* Wg, const void* Wu, const void* Wd, float* y,
                              int32_t* topk_idx, float* topk_w, float* logits, void* workspace, size_t ws_bytes,
@@ -184,11 +198,9 @@ beam_moe_status forward_impl(const beam_moe_shape* shape, const void* x, const v
         Wu = fp8->Wu;
         Wd = fp8->Wd;
     }
-    if (!x || !Wr || !bias || !Wg || !Wu || !Wd || (!y && !post)) return BEAM_MOE_ERR_INVALID_ARG;
-    if (!aligned(x) || !aligned(Wr) || !aligned(bias) || !aligned(Wg) || !aligned(Wu) || !aligned(Wd) ||
-        (y && !aligned(y)) || (norm_w && !aligned(norm_w)) || (topk_idx && !aligned(topk_idx)) ||
-        (topk_w && !aligned(topk_w)) || (logits && !aligned(logits)))
-        return BEAM_MOE_ERR_INVALID_ARG;
+    if ((st = check_tensors(x, norm_w, Wr, bias, Wg, Wu, Wd, y, topk_idx, topk_w, logits, post != nullptr)) !=
+        BEAM_MOE_OK)
+        return st;
     if (post && (st = check_post(s, *post)) != BEAM_MOE_OK) return st;
     if (s.T == 0) return BEAM_MOE_OK;
     const Layout L = layout(s);
@@ -411,6 +423,56 @@ beam_moe_status beam_moe_pack_weights(int64_t rows, int32_t K, const void* w, vo
     (void)hipGetLastError();
     beam::launch_pack_stream(w, packed, rows, K, (hipStream_t)stream);
     return hip_status();
+}
+
+}  // extern "C"
+
+// Scratch of beam_moe_forward_noalloc: the layer's workspace for callers that cannot allocate.
+// Each GPU the library runs on holds its own copy until the process ends. Host code never uses
+// the array's name as an address: the device address comes from hipGetSymbolAddress, looked up
+// once per device with that device current.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+void* g_scratch[kMaxDevices] = {};
+std::mutex g_scratch_mu;
+
+beam_moe_status scratch_of_current_device(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return BEAM_MOE_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return BEAM_MOE_ERR_HIP;
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return BEAM_MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+beam_moe_status beam_moe_forward_noalloc(const beam_moe_shape* shape, const void* x, const void* norm_w,
+                                         const float* Wr, const float* bias, const void* Wg, const void* Wu,
+                                         const void* Wd, float* y, int32_t* topk_idx, float* topk_w, float* logits,
+                                         void* stream) {
+    Shape s;
+    beam_moe_status st = to_shape(shape, &s);
+    if (st != BEAM_MOE_OK) return st;
+    if ((st = check_tensors(x, norm_w, Wr, bias, Wg, Wu, Wd, y, topk_idx, topk_w, logits, false)) != BEAM_MOE_OK)
+        return st;
+    if (s.T == 0) return BEAM_MOE_OK;
+    if (layout(s).total > kScratchBytes) return BEAM_MOE_ERR_WORKSPACE_TOO_SMALL;
+    void* ws = nullptr;
+    if ((st = scratch_of_current_device(&ws)) != BEAM_MOE_OK) return st;
+    // nothing in the scratch has to start at zero: the dispatch zeroes its own counters on every call
+    return forward_impl(shape, x, norm_w, Wr, bias, Wg, Wu, Wd, y, topk_idx, topk_w, logits, ws, kScratchBytes,
+                        stream, nullptr, nullptr);
 }
 
 const char* beam_moe_status_string(int32_t status) {

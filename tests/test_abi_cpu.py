@@ -300,3 +300,16 @@ def test_status_strings():
     assert moe.beam_moe_status_string(OK) == "ok"
     assert "workspace" in moe.beam_moe_status_string(WS_SMALL)
     assert moe.beam_moe_status_string(99) == "unknown status"
+
+
+def test_forward_noalloc_validates_before_launching():
+    """The no-allocation forward rejects bad arguments and shapes whose workspace exceeds its fixed
+    64 MiB scratch before it touches the GPU (no device is needed for any of these calls)."""
+    f = lambda s, *a: moe.beam_moe_forward_noalloc(s, *a, stream=0, check=False)
+    args = (A, None, A, A, A, A, A, A, None, None, None)
+    assert f(beam(T=512), *args) == WS_SMALL                      # 133 MiB of workspace
+    assert moe.beam_moe_workspace_bytes(beam(T=192)) <= 64 << 20   # the largest Beam batch it takes
+    assert f(beam(T=64), None, None, A, A, A, A, A, A, None, None, None) == INVALID     # x missing
+    assert f(beam(T=64), A, None, A, A, A, A, A, A + 4, None, None, None) == INVALID    # misaligned y
+    assert f(beam(T=64, d=5120 + 32), *args) == UNSUPPORTED
+    assert f(beam(T=0), *args) == OK
