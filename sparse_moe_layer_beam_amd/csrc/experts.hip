@@ -316,25 +316,32 @@ __global__ __launch_bounds__(256) void pack_stream_kernel(const u16* __restrict_
 // wave's token fragments are contiguous kilobytes like its weight fragments. In both kernels
 // the 4 waves of a block stream the same weight rows over four consecutive parts of k against
 // the four tiles, and their sums meet in LDS, added in part order. Measured on MI355X at
-// T = 64, d = 5120, I = 20480: 0.161 ms, against 0.190 ms with every k part written out and
-// added by a second kernel.
+// T = 64, d = 5120, I = 20480 (packed weights): 0.142-0.146 ms with each token fragment feeding four
+// weight fragments (two gate and two up 16-row blocks; four 16-row blocks of Wd), a 3-deep ring
+// and two blocks per CU, against 0.158 ms with two weight fragments per token fragment (1:1 -> 2:1
+// token bytes per weight byte from L2); 0.149 ms at depth 2 and three blocks per CU, 0.213 ms with
+// eight weight fragments (one wave per SIMD); 0.190 ms with every k part written out and added by a
+// second kernel. Results are bitwise the same in every form (the k order of each sum is unchanged).
 constexpr int kDT = 4;                   // token tiles (64 tokens)
 constexpr int kDD = 3;                   // ring depth of the dense streams
 constexpr int kDenseKsDN = 8;            // most k parts of the down pass across blocks
+constexpr int kDenseCG = 2;              // gate/up: 16-channel groups per block (2*kDenseCG weight rows per token fragment)
+constexpr int kDenseRB = 4;              // down: 16-row blocks of Wd per wave (kDenseRB weight rows per token fragment)
+constexpr int kDenseOcc = 2;             // blocks of 4 waves per CU the registers must allow
 
 // Adds the other waves' accumulators to wave 0's, in wave order. Returns true in wave 0.
 template <int NA>
-__device__ __forceinline__ bool dense_reduce(f32x4 (&red)[kWavesPerBlock][kDT][NA][64], int wave, int lane,
+__device__ __forceinline__ bool dense_reduce(f32x4 (&red)[kWavesPerBlock - 1][kDT][NA][64], int wave, int lane,
                                              f32x4 (&acc)[kDT][NA]) {
     if (wave != 0)
 #pragma unroll
         for (int m = 0; m < kDT; ++m)
 #pragma unroll
-            for (int q = 0; q < NA; ++q) red[wave][m][q][lane] = acc[m][q];
+            for (int q = 0; q < NA; ++q) red[wave - 1][m][q][lane] = acc[m][q];
     __syncthreads();
     if (wave != 0) return false;
 #pragma unroll
-    for (int j = 1; j < kWavesPerBlock; ++j)
+    for (int j = 0; j < kWavesPerBlock - 1; ++j)
 #pragma unroll
         for (int m = 0; m < kDT; ++m)
 #pragma unroll
@@ -346,56 +353,72 @@ __device__ __forceinline__ bool dense_reduce(f32x4 (&red)[kWavesPerBlock][kDT][N
 }
 
 // hp = bf16(silu(x . Wg[n]) * (x . Wu[n])) for all 64 token slots, written as packed token tiles
-// for the down pass. grid: I / 16; block: 4 waves, wave w streaming the gate and up rows of the
-// block's 16 channels over k part w of 4 (each token fragment feeds both).
-template <bool PK>
-__global__ __launch_bounds__(256, 3) void dense_gu_stream_kernel(const u16* __restrict__ xp, const u16* __restrict__ Wg,
-                                                              const u16* __restrict__ Wu, u16* __restrict__ hp, int d,
-                                                              int I) {
-    __shared__ f32x4 red[kWavesPerBlock][kDT][2][64];
+// for the down pass. grid: I / (16 CG); block: 4 waves, wave w streaming the gate and up rows of
+// the block's CG groups of 16 channels over k part w of 4: each token fragment feeds 2 CG weight
+// fragments.
+template <bool PK, int CG>
+__global__ __launch_bounds__(256, kDenseOcc) void dense_gu_stream_kernel(const u16* __restrict__ xp,
+                                                                      const u16* __restrict__ Wg,
+                                                                      const u16* __restrict__ Wu,
+                                                                      u16* __restrict__ hp, int d, int I) {
+    __shared__ f32x4 red[kWavesPerBlock - 1][kDT][2 * CG][64];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int n0 = blockIdx.x * 16;
+    const int n0 = blockIdx.x * 16 * CG;
     const int kl = d / kWavesPerBlock, k0 = wave * kl;
-    const size_t wo = PK ? ((size_t)n0 / 16 * (d / 32) * 64 + lane) * 8 + (size_t)k0 * 16
-                         : (size_t)(n0 + (lane & 15)) * d + (lane >> 4) * 8 + k0;
-    const u16* const a[2] = {Wg + wo, Wu + wo};
+    const u16* a[2 * CG];
+#pragma unroll
+    for (int g = 0; g < CG; ++g) {
+        const int ng = n0 + 16 * g;
+        const size_t wo = PK ? ((size_t)ng / 16 * (d / 32) * 64 + lane) * 8 + (size_t)k0 * 16
+                             : (size_t)(ng + (lane & 15)) * d + (lane >> 4) * 8 + k0;
+        a[g] = Wg + wo;
+        a[CG + g] = Wu + wo;
+    }
     const u16* xb[kDT];
 #pragma unroll
     for (int m = 0; m < kDT; ++m) xb[m] = xp + ((size_t)m * (d / 32) * 64 + lane) * 8 + (size_t)k0 * 16;
-    f32x4 acc[kDT][2];
+    f32x4 acc[kDT][2 * CG];
 #pragma unroll
-    for (int m = 0; m < kDT; ++m) acc[m][0] = acc[m][1] = f32x4{0, 0, 0, 0};
-    stream_core<2, kDT, kDD, PK, true>(a, xb, kl, acc);
-    if (!dense_reduce<2>(red, wave, lane, acc)) return;
-    // lane holds channels c .. c+3 (c = n0 + 4 (lane / 16)) of token slot 16 m + lane % 16; in
+    for (int m = 0; m < kDT; ++m)
+#pragma unroll
+        for (int q = 0; q < 2 * CG; ++q) acc[m][q] = f32x4{0, 0, 0, 0};
+    stream_core<2 * CG, kDT, kDD, PK, true>(a, xb, kl, acc);
+    if (!dense_reduce<2 * CG>(red, wave, lane, acc)) return;
+    // lane holds channels c .. c+3 (c = n0 + 16 g + 4 (lane / 16)) of token slot 16 m + lane % 16; in
     // the packed tiles they are elements c % 8 .. +3 of the 8-element chunk of k-step c / 32,
     // lane (lane % 16) + 16 ((c % 32) / 8)
-    const int c = n0 + 4 * (lane >> 4);
-    const int pl = (lane & 15) + 16 * ((c & 31) >> 3);
 #pragma unroll
-    for (int m = 0; m < kDT; ++m) {
-        const uint32_t lo = (uint32_t)f32_to_bf16(silu_mul(acc[m][0][0], acc[m][1][0])) |
-                            ((uint32_t)f32_to_bf16(silu_mul(acc[m][0][1], acc[m][1][1])) << 16);
-        const uint32_t hi = (uint32_t)f32_to_bf16(silu_mul(acc[m][0][2], acc[m][1][2])) |
-                            ((uint32_t)f32_to_bf16(silu_mul(acc[m][0][3], acc[m][1][3])) << 16);
-        *reinterpret_cast<uint2*>(hp + (((size_t)m * (I / 32) + c / 32) * 64 + pl) * 8 + (c & 7)) = make_uint2(lo, hi);
+    for (int g = 0; g < CG; ++g) {
+        const int c = n0 + 16 * g + 4 * (lane >> 4);
+        const int pl = (lane & 15) + 16 * ((c & 31) >> 3);
+#pragma unroll
+        for (int m = 0; m < kDT; ++m) {
+            const f32x4 gv = acc[m][g], uv = acc[m][CG + g];
+            const uint32_t lo = (uint32_t)f32_to_bf16(silu_mul(gv[0], uv[0])) |
+                                ((uint32_t)f32_to_bf16(silu_mul(gv[1], uv[1])) << 16);
+            const uint32_t hi = (uint32_t)f32_to_bf16(silu_mul(gv[2], uv[2])) |
+                                ((uint32_t)f32_to_bf16(silu_mul(gv[3], uv[3])) << 16);
+            *reinterpret_cast<uint2*>(hp + (((size_t)m * (I / 32) + c / 32) * 64 + pl) * 8 + (c & 7)) =
+                make_uint2(lo, hi);
+        }
     }
 }
 
 // part[kb][t][c] = sum over k part kb (of gridDim.y) of I for output channel c and token slot t.
-// grid: (d / 32, ks); block: 4 waves, wave w streaming the block's 32 rows of Wd (two 16-row
-// blocks, each token fragment feeding both) over quarter w of part kb.
-template <bool PK>
-__global__ __launch_bounds__(256, 3) void dense_dn_stream_kernel(const u16* __restrict__ hp, const u16* __restrict__ Wd,
-                                                              float* __restrict__ part, int d, int I) {
-    __shared__ f32x4 red[kWavesPerBlock][kDT][2][64];
+// grid: (d / (16 RB), ks); block: 4 waves, wave w streaming the block's RB 16-row blocks of Wd
+// (each token fragment feeding all of them) over quarter w of part kb.
+template <bool PK, int RB>
+__global__ __launch_bounds__(256, kDenseOcc) void dense_dn_stream_kernel(const u16* __restrict__ hp,
+                                                                      const u16* __restrict__ Wd,
+                                                                      float* __restrict__ part, int d, int I) {
+    __shared__ f32x4 red[kWavesPerBlock - 1][kDT][RB][64];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int n0 = blockIdx.x * 32;
+    const int n0 = blockIdx.x * 16 * RB;
     const int kb = blockIdx.y, kl = I / (int)gridDim.y / kWavesPerBlock;
     const int k0 = (kb * kWavesPerBlock + wave) * kl;
-    const u16* a[2];
+    const u16* a[RB];
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
+    for (int r = 0; r < RB; ++r) {
         const int nr = n0 + 16 * r;
         a[r] = Wd + (PK ? ((size_t)nr / 16 * (I / 32) * 64 + lane) * 8 + (size_t)k0 * 16
                         : (size_t)(nr + (lane & 15)) * I + (lane >> 4) * 8 + k0);
@@ -403,16 +426,18 @@ __global__ __launch_bounds__(256, 3) void dense_dn_stream_kernel(const u16* __re
     const u16* xb[kDT];
 #pragma unroll
     for (int m = 0; m < kDT; ++m) xb[m] = hp + ((size_t)m * (I / 32) * 64 + lane) * 8 + (size_t)k0 * 16;
-    f32x4 acc[kDT][2];
+    f32x4 acc[kDT][RB];
 #pragma unroll
-    for (int m = 0; m < kDT; ++m) acc[m][0] = acc[m][1] = f32x4{0, 0, 0, 0};
-    stream_core<2, kDT, kDD, PK, true>(a, xb, kl, acc);
-    if (!dense_reduce<2>(red, wave, lane, acc)) return;
+    for (int m = 0; m < kDT; ++m)
+#pragma unroll
+        for (int r = 0; r < RB; ++r) acc[m][r] = f32x4{0, 0, 0, 0};
+    stream_core<RB, kDT, kDD, PK, true>(a, xb, kl, acc);
+    if (!dense_reduce<RB>(red, wave, lane, acc)) return;
     const int tp = 16 * kDT;
 #pragma unroll
     for (int m = 0; m < kDT; ++m)
 #pragma unroll
-        for (int r = 0; r < 2; ++r)
+        for (int r = 0; r < RB; ++r)
             *reinterpret_cast<f32x4*>(part + ((size_t)kb * tp + 16 * m + (lane & 15)) * d + n0 + 16 * r +
                                       4 * (lane >> 4)) = acc[m][r];
 }
@@ -507,7 +532,10 @@ void launch_pack_stream(const void* W, void* P, int64_t rows, int K, hipStream_t
 }
 
 // every wave of both passes streams a whole number of 32-wide k-steps: d, I multiples of 128
-bool dense_stream_supports(int64_t T, int d, int I) { return T >= 1 && T <= 16 * kDT && d % 128 == 0 && I % 128 == 0; }
+bool dense_stream_supports(int64_t T, int d, int I) {
+    static_assert(128 % (16 * kDenseRB) == 0 && 128 % (16 * kDenseCG) == 0, "whole row blocks per block");
+    return T >= 1 && T <= 16 * kDT && d % 128 == 0 && I % 128 == 0;
+}
 
 size_t dense_stream_workspace_bytes(int64_t T, int d, int I) {
     (void)T;
@@ -530,18 +558,19 @@ void launch_dense_stream(int64_t T, int d, int I, bool packed, const void* x, co
     const int64_t xchunks = (int64_t)kDT * (d / 32) * 64;
     hipLaunchKernelGGL(pack_stream_kernel, dim3((unsigned)((xchunks + 255) / 256)), dim3(256), 0, st, (const u16*)x,
                        xp, (int64_t)tp, T, d);
+    const dim3 ggu((unsigned)(I / (16 * kDenseCG))), gdn((unsigned)(d / (16 * kDenseRB)), (unsigned)ks_dn);
     if (packed)
-        hipLaunchKernelGGL(dense_gu_stream_kernel<true>, dim3((unsigned)(I / 16)), dim3(256), 0, st, xp,
-                           (const u16*)Wg, (const u16*)Wu, hp, d, I);
+        hipLaunchKernelGGL((dense_gu_stream_kernel<true, kDenseCG>), ggu, dim3(256), 0, st, xp, (const u16*)Wg,
+                           (const u16*)Wu, hp, d, I);
     else
-        hipLaunchKernelGGL(dense_gu_stream_kernel<false>, dim3((unsigned)(I / 16)), dim3(256), 0, st, xp,
-                           (const u16*)Wg, (const u16*)Wu, hp, d, I);
+        hipLaunchKernelGGL((dense_gu_stream_kernel<false, kDenseCG>), ggu, dim3(256), 0, st, xp, (const u16*)Wg,
+                           (const u16*)Wu, hp, d, I);
     if (packed)
-        hipLaunchKernelGGL(dense_dn_stream_kernel<true>, dim3((unsigned)(d / 32), (unsigned)ks_dn), dim3(256), 0, st,
-                           hp, (const u16*)Wd, part_dn, d, I);
+        hipLaunchKernelGGL((dense_dn_stream_kernel<true, kDenseRB>), gdn, dim3(256), 0, st, hp, (const u16*)Wd, part_dn,
+                           d, I);
     else
-        hipLaunchKernelGGL(dense_dn_stream_kernel<false>, dim3((unsigned)(d / 32), (unsigned)ks_dn), dim3(256), 0, st,
-                           hp, (const u16*)Wd, part_dn, d, I);
+        hipLaunchKernelGGL((dense_dn_stream_kernel<false, kDenseRB>), gdn, dim3(256), 0, st, hp, (const u16*)Wd,
+                           part_dn, d, I);
     const int64_t ychunks = T * (d / 4);
     hipLaunchKernelGGL(dense_dn_finish_kernel, dim3((unsigned)((ychunks + 255) / 256)), dim3(256), 0, st, part_dn,
                        ks_dn, T, d, y);
