@@ -29,6 +29,10 @@
 //  * Weights in the packed layout (beam_moe_pack_weights) arrive in MFMA fragment order:
 //    each direct load copies one contiguous kilobyte (a 16-row block's 32-k step) and the
 //    fragment reads index it directly, no swizzle. Same results, same speed here.
+//
+// Packed weights whose k runs are multiples of 512 take a second kernel instead
+// (grouped_gemm_ws_kernel, below): the same items and arithmetic, weights streamed from
+// memory straight into registers and only the tokens staged in LDS.
 #include "common.h"
 #include "kernels.h"
 
@@ -378,6 +382,285 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(
     }
 }
 
+// ---- packed weights: weights streamed into registers, tokens through LDS --------------------
+//
+// The same work items as grouped_gemm_kernel (an expert's m-tile of up to 256 tokens x an n-block
+// of 256 weight rows), the same arithmetic (16x16x32 bf16 MFMAs over k in order into FP32
+// accumulators, the same epilogues), organised for packed weights:
+//  * eight waves, two per SIMD: wave w owns two 16-row weight blocks (gate/up: the gate rows and
+//    the up rows of channels n0 + 16 w .. +16; down: output channels n0 + 32 w .. +32) against
+//    every live token of the tile: up to 16 x 2 x 4 = 128 FP32 accumulators per lane.
+//  * each wave loads its weight fragments from memory straight into a ring of registers, WRW
+//    stages ahead; in the packed layout every fragment is one contiguous kilobyte. Each weight
+//    byte crosses the CU's vector memory path once: a stage moves 32 KB of weights and 32 KB of
+//    tokens through it. That path delivers about 64 bytes per clock per CU (measured on MI355X
+//    with L1-resident data), against 2048 MFMA clocks per full stage.
+//  * only the tokens pass through LDS: the eight waves load the live rows (direct-to-LDS, WDT
+//    stages ahead, the XOR swizzle of the kernel above) and every wave reads all of them: 256 KB
+//    of fragment reads per full stage, which LDS serves at about 200 bytes per clock.
+//  * every load is a buffer load (a per-lane offset fixed for the item, the stage in a scalar
+//    offset) and runs on every path, so the compiler counts its own waits on the ring precisely.
+constexpr int WM = 256;                   // tokens per tile
+constexpr int WK = 64;                    // k per stage
+constexpr int WNW = 8;                    // waves per block
+constexpr int WTB = WM * WK;              // bf16 of one token buffer (32 KB)
+constexpr int WNB = 4;                    // token buffers
+constexpr int WDT = WNB - 1;              // token stages loaded ahead
+constexpr int WPF = 4;                    // token fragments read from LDS ahead of their MFMAs
+constexpr int WUN = 8;                    // stages per loop iteration (divides the stage count)
+constexpr int kRsrcWord3 = 0x00020000;    // raw buffer, 32-bit data format (gfx9 V# word 3)
+
+// Waits until this wave's loads older than its N most recent have landed (the token loads of the
+// stage about to start among them) and its LDS reads are done, then meets the other waves.
+template <int N>
+__device__ __forceinline__ void ws_stage_wait() {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Keeps memory operations in program order on both sides of it, for the optimizer (the memory
+// clobber) and for the machine scheduler.
+__device__ __forceinline__ void ws_fence() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t ws_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+
+// Direct loads per wave per stage for LH live 16-token subtiles: 2 LH groups of 8 rows over
+// eight waves, the count rounded up (the spare loads repeat live rows into unread LDS rows).
+template <int LH>
+constexpr int ws_nt() {
+    return (2 * LH + WNW - 1) / WNW;
+}
+
+// Weight stages held in registers: four (64 VGPRs) up to 14 live subtiles; at 16 (128 FP32
+// accumulators) four would spill, so two.
+template <int LH>
+constexpr int ws_rw() {
+    return LH <= 14 ? 4 : 2;
+}
+
+// K loop and epilogue of one wave of a tile with LH live 16-token subtiles (even, 2..16).
+template <int MODE, int LH>
+__device__ __forceinline__ void ws_run(u16* lds, __amdgpu_buffer_rsrc_t trs, const uint32_t (&toff)[ws_nt<LH>()],
+                                       const __amdgpu_buffer_rsrc_t (&wrs)[2], int nstages, int wave, int lane,
+                                       int rows, size_t orow0, const int (&chq)[2], int Ndim,
+                                       const int32_t* __restrict__ pair_of_row, const float* __restrict__ topk_w,
+                                       void* __restrict__ out) {
+    constexpr int NT = ws_nt<LH>();           // token loads per stage
+    constexpr int NWL = 4;                    // weight loads per stage: 2 blocks x 2 k-halves
+    constexpr int WRW = ws_rw<LH>();
+    // loads issued after a stage's token loads, up to that stage: the weight refill issued with
+    // them, then WDT - 1 further stages of token loads and weight refills
+    constexpr int WAIT = NWL + (WDT - 1) * (NT + NWL);
+    static_assert(WAIT <= 63, "vmcnt range");
+    static_assert(WUN % WRW == 0, "ring slots repeat with the unrolled loop");
+    // after the prologue, the loads issued after stage 0's token loads
+    constexpr int WAIT0 = (WDT - 1) * NT + (WRW < WDT ? WRW : WDT) * NWL;
+    constexpr int PRO = WRW > WDT ? WRW : WDT;
+    f32x4 acc[LH][2];
+#pragma unroll
+    for (int i = 0; i < LH; ++i)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) acc[i][q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    bf16x8 wr[WRW][2][2];
+    const int last = nstages - 1;
+    const int lr = lane & 15, sw = lane & 7, c0 = lane >> 4;
+
+    auto tload = [&](int s) {
+        const int sc = min(s, last);
+        u16* const buf = lds + (s % WNB) * WTB;
+#pragma unroll
+        for (int i = 0; i < NT; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(trs, (lds_void*)(buf + 8 * (WNW * i + wave) * WK), 16, toff[i],
+                                                     sc * (WK * 2), 0, 0);
+    };
+    auto wload = [&](int s, int slot) {
+        const int sc = min(s, last);
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                wr[slot][q][j] = __builtin_bit_cast(
+                    bf16x8, __builtin_amdgcn_raw_buffer_load_b128(wrs[q], (uint32_t)lane * 16, (2 * sc + j) * 1024, 0));
+    };
+
+    // prologue, in the steady state's order: the loads of stages 0 .. PRO - 1 that run ahead
+#pragma unroll
+    for (int u = -PRO; u < 0; ++u) {
+        if (u + WDT >= 0) tload(u + WDT);
+        ws_fence();
+        if (u + WRW >= 0) wload(u + WRW, u + WRW);
+        ws_fence();
+    }
+    // fewer loads follow stage 0's tokens here than in the steady state: wait for them now
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(WAIT0) : "memory");
+    for (int s0 = 0; s0 < nstages; s0 += WUN) {
+#pragma unroll
+        for (int r = 0; r < WUN; ++r) {
+            const int s = s0 + r;
+            ws_stage_wait<WAIT>();
+            // the buffer loaded here, (s + WDT) % WNB = (s - 1) % WNB, was last read in stage s - 1
+            tload(s + WDT);
+            ws_fence();
+            const u16* const tb = lds + (s % WNB) * WTB;
+            bf16x8 xr[WPF];
+#pragma unroll
+            for (int f = 0; f < WPF; ++f)
+                xr[f] = *reinterpret_cast<const bf16x8*>(tb + (16 * (f % LH) + lr) * WK + ((4 * (f / LH) + c0) ^ sw) * 8);
+#pragma unroll
+            for (int f = 0; f < 2 * LH; ++f) {
+                const int i = f % LH, j = f / LH;
+                const bf16x8 x = xr[f % WPF];
+                const int g = f + WPF;
+                if (g < 2 * LH)
+                    xr[f % WPF] = *reinterpret_cast<const bf16x8*>(tb + (16 * (g % LH) + lr) * WK +
+                                                                   ((4 * (g / LH) + c0) ^ sw) * 8);
+#pragma unroll
+                for (int q = 0; q < 2; ++q) acc[i][q] = mfma16(wr[r % WRW][q][j], x, acc[i][q]);
+                ws_fence();
+            }
+            // slot r % WRW is free: the weights of stage s + WRW go there
+            wload(s + WRW, r % WRW);
+            ws_fence();
+        }
+    }
+    // the last (clamped, unused) loads must land before the block's LDS is released
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+    // Epilogue. acc[i][q][v]: token 16*i + lane%16 of the tile, channel chq[q] + 4*(lane/16) + v
+    // (gate/up: q = 0 gate and q = 1 up of the same channels).
+    const int rsub = 4 * (lane >> 4);
+#pragma unroll
+    for (int i = 0; i < LH; ++i) {
+        const int rr = 16 * i + lr;
+        if (rr >= rows) continue;
+        const size_t orow = orow0 + rr;
+        if constexpr (MODE == 0) {
+            u16* h = reinterpret_cast<u16*>(out);
+            const int ch = chq[0] + rsub;
+            if (ch >= Ndim) continue;
+            const uint32_t lo = (uint32_t)f32_to_bf16(silu_mul(acc[i][0][0], acc[i][1][0])) |
+                                ((uint32_t)f32_to_bf16(silu_mul(acc[i][0][1], acc[i][1][1])) << 16);
+            const uint32_t hi = (uint32_t)f32_to_bf16(silu_mul(acc[i][0][2], acc[i][1][2])) |
+                                ((uint32_t)f32_to_bf16(silu_mul(acc[i][0][3], acc[i][1][3])) << 16);
+            *reinterpret_cast<uint2*>(h + orow * Ndim + ch) = make_uint2(lo, hi);
+        } else {
+            float* y = reinterpret_cast<float*>(out);
+            const float wt = topk_w[pair_of_row[rr]];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int ch = chq[q] + rsub;
+                if (ch >= Ndim) continue;
+                *reinterpret_cast<float4*>(y + orow * Ndim + ch) =
+                    make_float4(wt * acc[i][q][0], wt * acc[i][q][1], wt * acc[i][q][2], wt * acc[i][q][3]);
+            }
+        }
+    }
+}
+
+template <int MODE, int LH>
+__device__ __forceinline__ void ws_item(u16* lds, const u16* __restrict__ act, uint32_t act_bytes,
+                                        const int32_t* __restrict__ sorted_pairs, int top_k, int beg, int m0, int rows,
+                                        int e, int n0, const u16* W0, const u16* W1, const float* __restrict__ topk_w,
+                                        void* __restrict__ out, int Kdim, int Ndim, int wave, int lane) {
+    // token offsets: load i of this wave covers rows 8(8i + wave) .. +8 of the tile, lane row
+    // + lane/8, global chunk (lane % 8) ^ (lane / 8); rows past the expert's segment repeat its last
+    constexpr int NT = ws_nt<LH>();
+    uint32_t toff[NT];
+    const int chunk = (lane & 7) ^ (lane >> 3);
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+        const int m = m0 + min(8 * (WNW * i + wave) + (lane >> 3), rows - 1);
+        uint32_t tr;
+        if constexpr (MODE == 0) tr = (uint32_t)(sorted_pairs[beg + m] / top_k);
+        else tr = (uint32_t)(beg + m);
+        toff[i] = (tr * (uint32_t)Kdim + 8u * chunk) * 2u;
+    }
+    const __amdgpu_buffer_rsrc_t trs = ws_rsrc(act, act_bytes);
+    // weight blocks: this wave's two 16-row blocks (gate/up: the gate and the up rows of 16
+    // channels; down: 32 output channels), each a resource of Kdim * 16 bf16; a block past Ndim
+    // reads the last block (discarded)
+    __amdgpu_buffer_rsrc_t wrs[2];
+    int chq[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const u16* W = W0;
+        int ch;
+        if constexpr (MODE == 0) {
+            ch = n0 + 16 * wave;
+            if (q == 1) W = W1;
+        } else {
+            ch = n0 + 32 * wave + 16 * q;
+        }
+        chq[q] = ch;
+        const size_t blk = ((size_t)e * Ndim + min(ch, Ndim - 16)) / 16;
+        wrs[q] = ws_rsrc(W + blk * (size_t)Kdim * 16, (uint32_t)Kdim * 32u);
+    }
+    ws_run<MODE, LH>(lds, trs, toff, wrs, Kdim / WK, wave, lane, rows, (size_t)(beg + m0), chq, Ndim,
+                     sorted_pairs + beg + m0, topk_w, out);
+}
+
+// MODE 0: out = h [P, I] bf16 = bf16(silu(act . Wg^T) * (act . Wu^T)), act = x rows gathered
+//         through sorted_pairs; W0 = Wg, W1 = Wu, packed [E*Ndim, Kdim].
+// MODE 1: out = y_perm [P, d] fp32 = w_pair * (act . Wd^T), act = h rows in sorted order; W0 = Wd.
+// act_bytes: the size of act (below 4 GiB: buffer offsets are 32-bit); Kdim a multiple of 512.
+// Work items and their claim as in grouped_gemm_kernel (the tile list of the dispatch).
+template <int MODE>
+__global__ __launch_bounds__(64 * WNW, 1) void grouped_gemm_ws_kernel(
+        const u16* __restrict__ act, uint32_t act_bytes, const int32_t* __restrict__ offsets,
+        const int32_t* __restrict__ sorted_pairs, const int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles_p,
+        // no __restrict__: loads through restrict-qualified read-only pointers are free to move past
+        // the fences that keep the weight and token loads in the order the waits count on
+        const u16* W0, const u16* W1, const float* __restrict__ topk_w, int top_k, void* __restrict__ out, int Kdim,
+        int Ndim, int n_nb) {
+    __shared__ __attribute__((aligned(1024))) u16 lds[WNB * WTB];
+    const int n_items = *n_tiles_p * n_nb;
+    const int per_xcd = (n_items + 7) / 8;
+    if ((int)blockIdx.x >= n_items + n_items / 4 + 64) return;
+    const int item = claim_item(n_tiles_p + 1 + 8 * MODE, blockIdx.x & 7, per_xcd, n_items, lds);
+    if (item < 0) return;
+    const int j = item / n_nb;
+    const int e = tiles[4 * j];
+    const int first = tiles[4 * j + 2];
+    const int cnt = tiles[4 * j + 3];
+    const int local = item - first * n_nb;
+    const int beg = offsets[e];
+    const int n_e = offsets[e + 1] - beg;
+    // the expert's n_nb x cnt items in groups of two n-blocks, m-tile-major inside a group
+    constexpr int GW = 2;
+    const int grp = local / (GW * cnt);
+    const int gw = min(GW, n_nb - grp * GW);
+    const int in = local - grp * GW * cnt;
+    const int mt = in / gw;
+    const int nb = grp * GW + (in - mt * gw);
+    const int m0 = mt * WM;
+    const int rows = min(WM, n_e - m0);
+    const int n0 = nb * (MODE == 0 ? 128 : 256);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // live 16-token subtiles, in pairs
+    const int lh = min(16, 2 * ((rows + 31) / 32));
+    switch (lh) {
+#define BEAM_WS_CASE(L)                                                                                         \
+    case L:                                                                                                     \
+        ws_item<MODE, L>(lds, act, act_bytes, sorted_pairs, top_k, beg, m0, rows, e, n0, W0, W1, topk_w, out,  \
+                         Kdim, Ndim, wave, lane);                                                               \
+        break;
+        BEAM_WS_CASE(2) BEAM_WS_CASE(4) BEAM_WS_CASE(6) BEAM_WS_CASE(8)
+        BEAM_WS_CASE(10) BEAM_WS_CASE(12) BEAM_WS_CASE(14) BEAM_WS_CASE(16)
+#undef BEAM_WS_CASE
+    }
+}
+
+// The weight-streaming form takes packed weights, stage counts that are multiples of WUN and
+// activations that 32-bit buffer offsets reach.
+bool ws_supports(const Shape& s, int Kdim, uint64_t act_bytes) {
+    return s.packed && Kdim % (WK * WUN) == 0 && act_bytes < ((uint64_t)1 << 32);
+}
+
 int max_items(const Shape& s, int n_nb) {
     const int64_t P = s.T * s.K;
     const int64_t max_tiles = (P + GM - 1) / GM + s.E;
@@ -397,6 +680,13 @@ void launch_gemm_swiglu(const Shape& s, const void* x, const int32_t* offsets, c
                         hipStream_t st) {
     const int n_nb = (s.I + GN / 2 - 1) / (GN / 2);
     const int blocks = (max_items(s, n_nb) + 7) / 8 * 8;
+    const uint64_t x_bytes = (uint64_t)s.T * s.d * 2;
+    if (ws_supports(s, s.d, x_bytes)) {
+        hipLaunchKernelGGL((grouped_gemm_ws_kernel<0>), dim3((unsigned)blocks), dim3(64 * WNW), 0, st, (const u16*)x,
+                           (uint32_t)x_bytes, offsets, sorted_pairs, tiles, n_tiles, (const u16*)Wg, (const u16*)Wu,
+                           nullptr, s.K, h, s.d, s.I, n_nb);
+        return;
+    }
 #define BEAM_GU(PK)                                                                                           \
     hipLaunchKernelGGL((grouped_gemm_kernel<0, false, PK>), dim3((unsigned)blocks), dim3(NT), 0, st,           \
                        (const u16*)x, offsets, sorted_pairs, tiles, n_tiles, (const u16*)Wg, (const u16*)Wu,  \
@@ -410,6 +700,13 @@ void launch_gemm_down(const Shape& s, const void* h, const int32_t* offsets, con
                       float* y_perm, hipStream_t st) {
     const int n_nb = (s.d + GN - 1) / GN;
     const int blocks = (max_items(s, n_nb) + 7) / 8 * 8;
+    const uint64_t h_bytes = (uint64_t)s.T * s.K * s.I * 2;
+    if (ws_supports(s, s.I, h_bytes)) {
+        hipLaunchKernelGGL((grouped_gemm_ws_kernel<1>), dim3((unsigned)blocks), dim3(64 * WNW), 0, st, (const u16*)h,
+                           (uint32_t)h_bytes, offsets, sorted_pairs, tiles, n_tiles, (const u16*)Wd, nullptr, topk_w,
+                           s.K, y_perm, s.I, s.d, n_nb);
+        return;
+    }
 #define BEAM_DN(PK)                                                                                           \
     hipLaunchKernelGGL((grouped_gemm_kernel<1, false, PK>), dim3((unsigned)blocks), dim3(NT), 0, st,           \
                        (const u16*)h, offsets, sorted_pairs, tiles, n_tiles, (const u16*)Wd, nullptr, topk_w, \
