@@ -81,15 +81,11 @@ T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws)
 
 beam_moe_status hip_status() { return hipGetLastError() == hipSuccess ? BEAM_MOE_OK : BEAM_MOE_ERR_HIP; }
 
-// Router into caller-visible buffers; x_in is already normed when a norm weight is used.
+// Router into caller-visible buffers; with a norm weight the router norms x into x_normed first.
 void run_route(const Shape& s, const Layout& L, const void* x, const void* norm_w, void* x_normed, const float* Wr,
                const float* bias, int32_t* idx, float* w, float* logits, void* ws, hipStream_t st) {
-    const void* xin = x;
-    if (norm_w) {
-        beam::launch_rmsnorm(s, x, norm_w, x_normed, st);
-        xin = x_normed;
-    }
-    beam::launch_router(s, xin, Wr, bias, at<void>(ws, L.wrs), at<float>(ws, L.zp), idx, w, logits, st);
+    beam::launch_router(s, x, norm_w, x_normed, Wr, bias, at<void>(ws, L.wrs), at<float>(ws, L.zp), idx, w, logits,
+                        st);
 }
 
 }  // namespace

@@ -21,10 +21,12 @@ void launch_rmsnorm(const Shape& s, const void* h, const void* w, void* x_out, h
 int router_ksplit(const Shape& s);
 size_t router_split_bytes(const Shape& s);
 size_t router_zp_floats(const Shape& s);
-// Logits, sigmoid, bias, group-limited top-k and weights for T tokens (x already normed).
+// Logits, sigmoid, bias, group-limited top-k and weights for T tokens. With norm_w the input h
+// is first normed into x_normed (pre-MLP RMSNorm, in the launch that splits the router weight
+// when the route has one), which the router then reads; without it h is x.
 // wrs: scratch of router_split_bytes(s); z_part: scratch of router_zp_floats(s) floats.
-void launch_router(const Shape& s, const void* x, const float* Wr, const float* bias, void* wrs, float* z_part,
-                   int32_t* idx, float* w, float* logits, hipStream_t st);
+void launch_router(const Shape& s, const void* h, const void* norm_w, void* x_normed, const float* Wr,
+                   const float* bias, void* wrs, float* z_part, int32_t* idx, float* w, float* logits, hipStream_t st);
 
 // Dispatch (dispatch.hip)
 constexpr int kChunkPairs = 1024;

@@ -16,9 +16,8 @@ namespace {
 // Pre-MLP RMSNorm, one 256-thread block per token. Done in FP64 (the pages ask for at
 // least FP32): the bf16 rounding of x is then a function of h and w alone, independent
 // of the reduction order, so every consumer of x sees the same bits.
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const u16* __restrict__ h, const u16* __restrict__ w,
-                                                      u16* __restrict__ x, int d, double eps) {
-    const int64_t t = blockIdx.x;
+__device__ __forceinline__ void rmsnorm_row(const u16* __restrict__ h, const u16* __restrict__ w,
+                                            u16* __restrict__ x, int d, double eps, int64_t t) {
     const u16* hr = h + t * d;
     double ss = 0.0;
     for (int c = threadIdx.x * 8; c < d; c += 256 * 8) {
@@ -50,6 +49,11 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const u16* __restrict__ h,
         }
         *reinterpret_cast<uint4*>(x + t * d + c) = make_uint4(o[0], o[1], o[2], o[3]);
     }
+}
+
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const u16* __restrict__ h, const u16* __restrict__ w,
+                                                      u16* __restrict__ x, int d, double eps) {
+    rmsnorm_row(h, w, x, d, eps, blockIdx.x);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -299,11 +303,11 @@ __device__ __forceinline__ void split3(float w, uint32_t& hi, uint32_t& mid, uin
     lo = (uint32_t)f32_to_bf16(r1 - m);
 }
 
-// Wr [d, E] fp32 -> WrS [3][E][d] bf16 (expert-major, k contiguous: the MFMA B-operand layout).
-__global__ __launch_bounds__(256) void router_split_kernel(const float* __restrict__ Wr, u16* __restrict__ WrS,
-                                                           int d, int E) {
+// Wr [d, E] fp32 -> WrS [3][E][d] bf16 (expert-major, k contiguous: the MFMA B-operand layout),
+// the 64 x 64 tile (k0, e0).
+__device__ __forceinline__ void split_tile(const float* __restrict__ Wr, u16* __restrict__ WrS, int d, int E,
+                                           int k0, int e0) {
     __shared__ float tile[64][65];
-    const int k0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
     for (int i = threadIdx.x; i < 64 * 16; i += 256) {
         const int kk = i >> 4, ec = (i & 15) * 4;
         const float4 v = *reinterpret_cast<const float4*>(Wr + (size_t)(k0 + kk) * E + e0 + ec);
@@ -326,6 +330,27 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float* __restri
             *reinterpret_cast<uint4*>(WrS + ((size_t)pl * E + e0 + e) * d + k0 + kc) =
                 make_uint4(p[pl][0], p[pl][1], p[pl][2], p[pl][3]);
     }
+}
+
+__global__ __launch_bounds__(256) void router_split_kernel(const float* __restrict__ Wr, u16* __restrict__ WrS,
+                                                           int d, int E) {
+    split_tile(Wr, WrS, d, E, blockIdx.x * 64, blockIdx.y * 64);
+}
+
+// The two passes that precede the router product when the layer opens with the pre-MLP
+// RMSNorm, in one launch: blocks [0, T) norm one token each (x = bf16(h * r * w), the x the
+// router and the experts read), blocks [T, T + (d/64)(E/64)) split one 64 x 64 tile of Wr.
+__global__ __launch_bounds__(256) void router_prep_kernel(const u16* __restrict__ h, const u16* __restrict__ w,
+                                                          u16* __restrict__ x, double eps, int64_t T,
+                                                          const float* __restrict__ Wr, u16* __restrict__ WrS,
+                                                          int d, int E) {
+    const int64_t b = blockIdx.x;
+    if (b < T) {
+        rmsnorm_row(h, w, x, d, eps, b);
+        return;
+    }
+    const int tile = (int)(b - T), nk = d / 64;
+    split_tile(Wr, WrS, d, E, (tile % nk) * 64, (tile / nk) * 64);
 }
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -514,22 +539,31 @@ size_t router_zp_floats(const Shape& s) {
     return (size_t)router_ksplit(s) * s.T * s.E;
 }
 
-void launch_router(const Shape& s, const void* x, const float* Wr, const float* bias, void* wrs, float* z_part,
-                   int32_t* idx, float* w, float* logits, hipStream_t st) {
+void launch_router(const Shape& s, const void* h, const void* norm_w, void* x_normed, const float* Wr,
+                   const float* bias, void* wrs, float* z_part, int32_t* idx, float* w, float* logits, hipStream_t st) {
     const int gks = router_gemm_ks(s);
     const int ks = gks ? gks : router_ksplit(s);
     const int P = gks ? 3 : 1;
     const int epl = s.E <= 64 ? 1 : s.E / 64;
     const unsigned tb = (unsigned)((s.T + 63) / 64);
-    if (gks) {
+    const bool split = gks || (router_uses_mfma(s) && !((int64_t)tb * ks <= 256 && ks > 1));
+    // the router reads x: the input itself, or the normed copy made here (with the weight split
+    // when there is one, in the same launch)
+    const void* x = norm_w ? x_normed : h;
+    if (split && norm_w) {
+        const unsigned nb = (unsigned)(s.T + (int64_t)(s.d / 64) * (s.E / 64));
+        hipLaunchKernelGGL(router_prep_kernel, dim3(nb), dim3(256), 0, st, (const u16*)h, (const u16*)norm_w,
+                           (u16*)x_normed, (double)s.eps, s.T, Wr, (u16*)wrs, s.d, s.E);
+    } else if (split) {
         hipLaunchKernelGGL(router_split_kernel, dim3((unsigned)(s.d / 64), (unsigned)(s.E / 64)), dim3(256), 0, st,
                            Wr, (u16*)wrs, s.d, s.E);
+    } else if (norm_w) {
+        launch_rmsnorm(s, h, norm_w, x_normed, st);
+    }
+    if (gks) {
         launch_gemm_router(s, x, wrs, z_part, gks, st);
     } else if (router_uses_mfma(s)) {
-        const bool small = (int64_t)tb * ks <= 256 && ks > 1;
-        if (!small)
-            hipLaunchKernelGGL(router_split_kernel, dim3((unsigned)(s.d / 64), (unsigned)(s.E / 64)), dim3(256), 0,
-                               st, Wr, (u16*)wrs, s.d, s.E);
+        const bool small = !split;
 #define BEAM_RMMA(NTW, F)                                                                                        \
     hipLaunchKernelGGL((router_mfma_kernel<NTW, F>), dim3(tb, (unsigned)ks), dim3(256), 0, st, (const u16*)x,     \
                        (const u16*)wrs, z_part, s.T, s.d, s.E, s.d / ks, s.G, s.KG, s.K, s.S, s.norm, bias, idx, w, \
