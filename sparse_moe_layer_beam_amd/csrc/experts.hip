@@ -322,11 +322,17 @@ __global__ __launch_bounds__(256) void pack_stream_kernel(const u16* __restrict_
 // token bytes per weight byte from L2); 0.149 ms at depth 2 and three blocks per CU, 0.213 ms with
 // eight weight fragments (one wave per SIMD); 0.190 ms with every k part written out and added by a
 // second kernel. Results are bitwise the same in every form (the k order of each sum is unchanged).
+// With the down pass in one round (dense_rb_dn): 0.133 ms; gate/up 87 us for 419 MB, down 41 us,
+// token packing 6 us, the k-part sum 5 us. Tried on the gate/up pass without gain: ring depth 4
+// and 5 (0.140, 0.150 ms), each block starting its k walk at a different step (0.133), the
+// unit's weight blocks read as if interleaved per k step (0.133), and the launch's last partial
+// round split into k quarters added by the last block to finish (-1 us, not kept). A copy that
+// skips the token fragment reloads runs 0.115 ms: the token reads, not the weight stream's
+// DRAM pattern, hold this pass at ~4.8 TB/s.
 constexpr int kDT = 4;                   // token tiles (64 tokens)
 constexpr int kDD = 3;                   // ring depth of the dense streams
 constexpr int kDenseKsDN = 8;            // most k parts of the down pass across blocks
 constexpr int kDenseCG = 2;              // gate/up: 16-channel groups per block (2*kDenseCG weight rows per token fragment)
-constexpr int kDenseRB = 4;              // down: 16-row blocks of Wd per wave (kDenseRB weight rows per token fragment)
 constexpr int kDenseOcc = 2;             // blocks of 4 waves per CU the registers must allow
 
 // Adds the other waves' accumulators to wave 0's, in wave order. Returns true in wave 0.
@@ -466,6 +472,12 @@ int dense_ks_dn(int I) {
     return ks;
 }
 
+// 16-row blocks of Wd per down block (each token fragment feeds them all): five when d allows,
+// else four. At d = 5120 five give 64 x 8 = 512 blocks, one round at two blocks per CU on
+// MI355X; four gave 640, whose last 128 ran as a second round: down pass 47.4 -> 40.9 us at
+// T = 64, I = 20480 (bitwise the same y).
+int dense_rb_dn(int d) { return d % (16 * 5) == 0 ? 5 : 4; }
+
 }  // namespace
 
 // Path choice from the average number of tokens per expert: up to 16 the weight-streaming
@@ -533,7 +545,7 @@ void launch_pack_stream(const void* W, void* P, int64_t rows, int K, hipStream_t
 
 // every wave of both passes streams a whole number of 32-wide k-steps: d, I multiples of 128
 bool dense_stream_supports(int64_t T, int d, int I) {
-    static_assert(128 % (16 * kDenseRB) == 0 && 128 % (16 * kDenseCG) == 0, "whole row blocks per block");
+    static_assert(128 % (16 * kDenseCG) == 0, "whole row blocks per block");
     return T >= 1 && T <= 16 * kDT && d % 128 == 0 && I % 128 == 0;
 }
 
@@ -548,7 +560,7 @@ void launch_dense_stream(int64_t T, int d, int I, bool packed, const void* x, co
                          const void* Wd, float* y, void* ws, hipStream_t st) {
     const size_t tp = 16 * kDT;
     auto up = [](size_t v) { return (v + 255) / 256 * 256; };
-    const int ks_dn = dense_ks_dn(I);
+    const int ks_dn = dense_ks_dn(I), rb = dense_rb_dn(d);
     char* w = static_cast<char*>(ws);
     u16* xp = reinterpret_cast<u16*>(w);
     w += up(tp * d * 2);
@@ -558,19 +570,21 @@ void launch_dense_stream(int64_t T, int d, int I, bool packed, const void* x, co
     const int64_t xchunks = (int64_t)kDT * (d / 32) * 64;
     hipLaunchKernelGGL(pack_stream_kernel, dim3((unsigned)((xchunks + 255) / 256)), dim3(256), 0, st, (const u16*)x,
                        xp, (int64_t)tp, T, d);
-    const dim3 ggu((unsigned)(I / (16 * kDenseCG))), gdn((unsigned)(d / (16 * kDenseRB)), (unsigned)ks_dn);
+    const dim3 ggu((unsigned)(I / (16 * kDenseCG))), gdn((unsigned)(d / (16 * rb)), (unsigned)ks_dn);
     if (packed)
         hipLaunchKernelGGL((dense_gu_stream_kernel<true, kDenseCG>), ggu, dim3(256), 0, st, xp, (const u16*)Wg,
                            (const u16*)Wu, hp, d, I);
     else
         hipLaunchKernelGGL((dense_gu_stream_kernel<false, kDenseCG>), ggu, dim3(256), 0, st, xp, (const u16*)Wg,
                            (const u16*)Wu, hp, d, I);
-    if (packed)
-        hipLaunchKernelGGL((dense_dn_stream_kernel<true, kDenseRB>), gdn, dim3(256), 0, st, hp, (const u16*)Wd, part_dn,
-                           d, I);
-    else
-        hipLaunchKernelGGL((dense_dn_stream_kernel<false, kDenseRB>), gdn, dim3(256), 0, st, hp, (const u16*)Wd,
-                           part_dn, d, I);
+#define BEAM_DDN(PK, RB)                                                                                       \
+    hipLaunchKernelGGL((dense_dn_stream_kernel<PK, RB>), gdn, dim3(256), 0, st, hp, (const u16*)Wd, part_dn, d, I)
+    if (rb == 5) {
+        if (packed) BEAM_DDN(true, 5); else BEAM_DDN(false, 5);
+    } else {
+        if (packed) BEAM_DDN(true, 4); else BEAM_DDN(false, 4);
+    }
+#undef BEAM_DDN
     const int64_t ychunks = T * (d / 4);
     hipLaunchKernelGGL(dense_dn_finish_kernel, dim3((unsigned)((ychunks + 255) / 256)), dim3(256), 0, st, part_dn,
                        ks_dn, T, d, y);
