@@ -113,6 +113,38 @@ def test_forward_packed_against_oracle_mid():
     assert err <= P.Y_TOL * rms
 
 
+# d = I = 512: both grouped GEMMs take the weight-streaming form on packed weights (k runs of 512)
+# and the LDS-staged form on row-major ones; four hot experts get several 256-token m-tiles each,
+# the last ragged, and the cold ones partial tiles of every live-subtile count
+WS_MID = recipes.Workload(42, "ws_mid_T1500", T=1500, d=512, E=64, n_group=8, topk_group=4, top_k=8, I=512,
+                          hot_experts=4, hot_bias=0.5)
+
+
+def test_weight_streaming_gemms_every_token():
+    """The weight-streaming grouped GEMMs (both passes) against the oracle on every token, and
+    bitwise equal to the LDS-staged GEMMs on the same values in the row-major layout."""
+    w = WS_MID
+    print("case packed", w.name, flush=True)
+    t = synth.device_inputs(w)
+    rm = _forward(w, t, moe.WEIGHTS_ROW_MAJOR, (t["Wg"], t["Wu"], t["Wd"]))
+    pk = _forward(w, t, moe.WEIGHTS_PACKED, moe.pack_expert_weights(t["Wg"], t["Wu"], t["Wd"]))
+    for a, b in zip(rm, pk):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    y, idx, wt = pk
+    counts = np.bincount(idx.reshape(-1), minlength=w.E)
+    assert counts.max() > 2 * 256 and (counts[counts > 0] % 256).min() < 32   # several m-tiles; small tails
+    x, Wr, b = _oracle_inputs(w)
+    idx_ref, w_ref, gap, z_ref = oracle.route(x, Wr, b, w.n_group, w.topk_group, w.top_k, w.scale,
+                                              w.norm_topk_prob, want_logits=True)
+    same = P.compare_routing(idx, wt, idx_ref, w_ref, gap, z_ref, b, w.n_group, w.topk_group, w.top_k)
+    rows = np.nonzero(same)[0]
+    ref = oracle.moe_rows(x[rows], idx_ref[rows], w_ref[rows], _experts_host(w, range(w.E)), w.E)
+    err, rms = P.output_error(y[rows], ref)
+    print("%s: compared %d of %d tokens, max|dy| %.3e, rms %.3e" % (w.name, len(rows), w.T, err, rms))
+    assert len(rows) >= w.T - 4
+    assert err <= P.Y_TOL * rms
+
+
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4])
 def test_forward_packed_bitwise_beam(cfg):
     """Every Beam workload (decode streams; prefill, skewed and large-chunk grouped GEMMs): packed
