@@ -329,7 +329,8 @@ __global__ __launch_bounds__(256) void pack_stream_kernel(const u16* __restrict_
 // round split into k quarters added by the last block to finish (-1 us, not kept). A copy that
 // skips the token fragment reloads runs 0.115 ms: the token reads, not the weight stream's
 // DRAM pattern, hold this pass at ~4.8 TB/s. Reading x rows directly (16 rows x 64 B per
-// fragment, no packing launch) ran 0.163 ms against 0.136.
+// fragment, no packing launch) ran 0.163 ms against 0.136; the k-part sum folded into the down
+// pass (the last block of a column group adds the parts) 0.1375 against 0.1355.
 constexpr int kDT = 4;                   // token tiles (64 tokens)
 constexpr int kDD = 3;                   // ring depth of the dense streams
 constexpr int kDenseKsDN = 8;            // most k parts of the down pass across blocks
