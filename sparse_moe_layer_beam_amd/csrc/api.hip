@@ -232,14 +232,14 @@ beam_moe_status forward_impl(const beam_moe_shape* shape, const void* x, const v
         beam::launch_swiglu(s, xin, off, sp, tiles, ntiles, Wg, Wu, h, hs);
     mark(3);
     if (fp8)
-        beam::launch_down_fp8(s, h, off, sp, w, fp8->Wd, fp8->sd, yp, hs);
+        beam::launch_down_fp8(s, h, off, fp8->Wd, fp8->sd, yp, hs);
     else
-        beam::launch_down(s, h, off, sp, w, tiles, ntiles, Wd, yp, hs);
+        beam::launch_down(s, h, off, sp, tiles, ntiles, Wd, yp, hs);
     mark(4);
     if (post)
-        beam::launch_combine_post_residual(s, yp, pr, post->w, post->layer, post->resid, post->resid_out, y, hs);
+        beam::launch_combine_post_residual(s, yp, pr, w, post->w, post->layer, post->resid, post->resid_out, y, hs);
     else
-        beam::launch_combine(s, yp, pr, y, hs);
+        beam::launch_combine(s, yp, pr, w, y, hs);
     mark(5);
     return hip_status();
 }
@@ -404,9 +404,9 @@ beam_moe_status beam_moe_experts_share(const beam_moe_shape* shape, int32_t e_be
     mark(2);
     beam::launch_swiglu(sl, x, off, sp, tiles, ntiles, Wg, Wu, h, hs);
     mark(3);
-    beam::launch_down(sl, h, off, sp, topk_w, tiles, ntiles, Wd, yp, hs);
+    beam::launch_down(sl, h, off, sp, tiles, ntiles, Wd, yp, hs);
     mark(4);
-    beam::launch_combine(sl, yp, pr, y_part, hs);
+    beam::launch_combine(sl, yp, pr, topk_w, y_part, hs);
     mark(5);
     return hip_status();
 }

@@ -210,14 +210,13 @@ __global__ __launch_bounds__(256, kGuOcc) void swiglu_stream_kernel(const u16* _
     }
 }
 
-// y_perm[beg+m, c] = w_pair * (h[beg+m] . Wd[e,c]) for the tokens m of expert e.
+// y_perm[beg+m, c] = h[beg+m] . Wd[e,c] for the tokens m of expert e (the combine applies the
+// routing weight).
 // grid: (ceil(d / (16 * 4 / KS)), E); block: 4 waves; the KS waves of a 16-row group of Wd
 // each stream a 1/KS part of k, as in the gate/up kernel.
 template <int KS, bool PK>
 __global__ __launch_bounds__(256, kDnOcc) void down_stream_kernel(const u16* __restrict__ h,
                                                           const int32_t* __restrict__ offsets,
-                                                          const int32_t* __restrict__ sorted_pairs,
-                                                          const float* __restrict__ topk_w,
                                                           const u16* __restrict__ Wd, float* __restrict__ y_perm,
                                                           int d, int I) {
     __shared__ f32x4 part[kWavesPerBlock][1][kMT][64];
@@ -250,11 +249,9 @@ __global__ __launch_bounds__(256, kDnOcc) void down_stream_kernel(const u16* __r
             for (int mt = 0; mt < kMT; ++mt) {
                 const int m = mb + 16 * mt + r16;
                 if (mt >= ntile || m >= n_e) continue;
-                const float wt = topk_w[sorted_pairs[beg + m]];
                 const int c = n0 + (lane >> 4) * 4;
                 const f32x4 v = acc[0][mt][0];
-                *reinterpret_cast<float4*>(y_perm + (size_t)(beg + m) * d + c) =
-                    make_float4(wt * v[0], wt * v[1], wt * v[2], wt * v[3]);
+                *reinterpret_cast<float4*>(y_perm + (size_t)(beg + m) * d + c) = make_float4(v[0], v[1], v[2], v[3]);
             }
         if constexpr (KS > 1) __syncthreads();
     }
@@ -263,9 +260,14 @@ __global__ __launch_bounds__(256, kDnOcc) void down_stream_kernel(const u16* __r
 // y[t] = sum over slots j = 0..K-1, in that order, of y_perm[pair_rank[t*K + j]]; slots with
 // pair_rank -1 (an expert this call does not hold: expert-parallel share) add nothing, and a
 // row with no slot left is 0. grid: (T, ceil(d / 1024)); each thread owns one float4 of the row.
+// y[t] = sum over the slots j, in slot order, of topk_w[t, j] * y_perm[rank(t, j)] (each product
+// rounded to FP32 on its own: no contraction into FMA). A rank of -1 (a slot outside an
+// expert-parallel share) contributes nothing.
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y_perm,
-                                                      const int32_t* __restrict__ pair_rank, int K, int d,
+                                                      const int32_t* __restrict__ pair_rank,
+                                                      const float* __restrict__ topk_w, int K, int d,
                                                       float* __restrict__ y) {
+#pragma clang fp contract(off)
     const int64_t t = blockIdx.x;
     const int c = (blockIdx.y * 256 + threadIdx.x) * 4;
     if (c >= d) return;
@@ -278,7 +280,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
         if (rk[j] >= 0) {
             // each y_perm element is read once (non-temporal: T=8192 0.305 -> 0.267 ms on MI355X)
             const u32x4 r = ld_once(y_perm + (size_t)rk[j] * d + c);
-            v[j] = make_float4(__uint_as_float(r.x), __uint_as_float(r.y), __uint_as_float(r.z), __uint_as_float(r.w));
+            const float wt = topk_w[t * K + j];
+            v[j] = make_float4(wt * __uint_as_float(r.x), wt * __uint_as_float(r.y), wt * __uint_as_float(r.z),
+                               wt * __uint_as_float(r.w));
         }
     float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     bool first = true;
@@ -514,10 +518,9 @@ void launch_swiglu(const Shape& s, const void* x, const int32_t* offsets, const 
 }
 
 void launch_down(const Shape& s, const void* h, const int32_t* offsets, const int32_t* sorted_pairs,
-                 const float* topk_w, const int32_t* tiles, int32_t* n_tiles, const void* Wd,
-                 float* y_perm, hipStream_t st) {
+                 const int32_t* tiles, int32_t* n_tiles, const void* Wd, float* y_perm, hipStream_t st) {
     if (experts_tiled(s)) {
-        launch_gemm_down(s, h, offsets, sorted_pairs, topk_w, tiles, n_tiles, Wd, y_perm, st);
+        launch_gemm_down(s, h, offsets, sorted_pairs, tiles, n_tiles, Wd, y_perm, st);
         return;
     }
     const int ks = s.I % (32 * kDnKsplit) == 0 ? kDnKsplit : 1;
@@ -525,7 +528,7 @@ void launch_down(const Shape& s, const void* h, const int32_t* offsets, const in
     const dim3 grid((unsigned)((s.d + per_block - 1) / per_block), (unsigned)s.E);
 #define BEAM_DN(KS, PK)                                                                                       \
     hipLaunchKernelGGL((down_stream_kernel<KS, PK>), grid, dim3(256), 0, st, (const u16*)h, offsets,           \
-                       sorted_pairs, topk_w, (const u16*)Wd, y_perm, s.d, s.I)
+                       (const u16*)Wd, y_perm, s.d, s.I)
     if (ks == kDnKsplit) {
         if (s.packed) BEAM_DN(kDnKsplit, true); else BEAM_DN(kDnKsplit, false);
     } else {
@@ -534,9 +537,10 @@ void launch_down(const Shape& s, const void* h, const int32_t* offsets, const in
 #undef BEAM_DN
 }
 
-void launch_combine(const Shape& s, const float* y_perm, const int32_t* pair_rank, float* y, hipStream_t st) {
+void launch_combine(const Shape& s, const float* y_perm, const int32_t* pair_rank, const float* topk_w, float* y,
+                    hipStream_t st) {
     hipLaunchKernelGGL(combine_kernel, dim3((unsigned)s.T, (unsigned)((s.d + 1023) / 1024)), dim3(256), 0, st, y_perm,
-                       pair_rank, s.K, s.d, y);
+                       pair_rank, topk_w, s.K, s.d, y);
 }
 
 void launch_pack_stream(const void* W, void* P, int64_t rows, int K, hipStream_t st) {

@@ -210,14 +210,13 @@ __global__ __launch_bounds__(256) void swiglu_fp8_kernel(const u16* __restrict__
     }
 }
 
-// y_perm[beg+m, n] = w_pair * (h[beg+m] . Wd[e,n]) with fp8 Wd. grid: (ceil(d / (64 * kDnRB)), E);
+// y_perm[beg+m, n] = h[beg+m] . Wd[e,n] with fp8 Wd (the combine applies the routing weight).
+// grid: (ceil(d / (64 * kDnRB)), E);
 // block: 4 waves, each streaming kDnRB blocks of 16 output channels whose rows share the
 // activation fragments (one 16-row block of 1-byte codes is only a 40 KB stream at I = 2560).
 constexpr int kDnRB = 2;
 template <bool PK>
 __global__ __launch_bounds__(256) void down_fp8_kernel(const u16* __restrict__ h, const int32_t* __restrict__ offsets,
-                                                       const int32_t* __restrict__ sorted_pairs,
-                                                       const float* __restrict__ topk_w,
                                                        const uint8_t* __restrict__ Wd, const uint8_t* __restrict__ sd,
                                                        float* __restrict__ y_perm, int d, int I) {
     const int e = blockIdx.y;
@@ -243,11 +242,10 @@ __global__ __launch_bounds__(256) void down_fp8_kernel(const u16* __restrict__ h
         for (int b = 0; b < kDnRB; ++b) acc[0][b] = f32x4{0, 0, 0, 0};
         stream_fp8<kDnRB, 1, PK>(wq, ws, hp, I, c, acc);
         if (mb + r < n_e) {
-            const float wt = topk_w[sorted_pairs[beg + mb + r]];
 #pragma unroll
             for (int b = 0; b < kDnRB; ++b)
                 *reinterpret_cast<float4*>(y_perm + (size_t)(beg + mb + r) * d + n0 + 16 * b + 4 * c) =
-                    make_float4(wt * acc[0][b][0], wt * acc[0][b][1], wt * acc[0][b][2], wt * acc[0][b][3]);
+                    make_float4(acc[0][b][0], acc[0][b][1], acc[0][b][2], acc[0][b][3]);
         }
     }
 }
@@ -273,12 +271,12 @@ void launch_swiglu_fp8(const Shape& s, const void* x, const int32_t* offsets, co
 #undef BEAM_GU8
 }
 
-void launch_down_fp8(const Shape& s, const void* h, const int32_t* offsets, const int32_t* sorted_pairs,
-                     const float* topk_w, const void* Wd8, const void* sd, float* y_perm, hipStream_t st) {
+void launch_down_fp8(const Shape& s, const void* h, const int32_t* offsets, const void* Wd8, const void* sd,
+                     float* y_perm, hipStream_t st) {
 #define BEAM_DN8(PK)                                                                                          \
     hipLaunchKernelGGL((down_fp8_kernel<PK>), dim3((unsigned)((s.d + 64 * kDnRB - 1) / (64 * kDnRB)), (unsigned)s.E), \
                        dim3(256), 0, st,                                                                      \
-                       static_cast<const u16*>(h), offsets, sorted_pairs, topk_w, static_cast<const uint8_t*>(Wd8), \
+                       static_cast<const u16*>(h), offsets, static_cast<const uint8_t*>(Wd8),                 \
                        static_cast<const uint8_t*>(sd), y_perm, s.d, s.I)
     if (s.packed) BEAM_DN8(true); else BEAM_DN8(false);
 #undef BEAM_DN8

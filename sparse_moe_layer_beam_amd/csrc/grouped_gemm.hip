@@ -117,7 +117,6 @@ __device__ __forceinline__ void stage_mma(const u16* tb, const u16* wb, int tok0
 template <int MODE, int LIVE, bool PK>
 __device__ __forceinline__ void gemm_run(u16* lds, const u16* const (&src)[DMA], int nstages, int wave, int lane,
                                          int tok0, const int (&wrow)[4], int rows, size_t orow0, int c0, int Ndim,
-                                         const int32_t* __restrict__ pair_of_row, const float* __restrict__ topk_w,
                                          void* __restrict__ out) {
     f32x4 acc[8][4];
 #pragma unroll
@@ -177,13 +176,12 @@ __device__ __forceinline__ void gemm_run(u16* lds, const u16* const (&src)[DMA],
             }
         } else {
             float* y = reinterpret_cast<float*>(out);
-            const float wt = topk_w ? topk_w[pair_of_row[r]] : 1.0f;   // NULL: dense MLP, weight 1
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int ch = c0 + 16 * q + rsub;
                 if (ch >= Ndim) continue;
                 *reinterpret_cast<float4*>(y + orow * Ndim + ch) =
-                    make_float4(wt * acc[i][q][0], wt * acc[i][q][1], wt * acc[i][q][2], wt * acc[i][q][3]);
+                    make_float4(acc[i][q][0], acc[i][q][1], acc[i][q][2], acc[i][q][3]);
             }
         }
     }
@@ -243,7 +241,7 @@ template <int MODE, bool DENSE, bool PK>
 __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(
         const u16* __restrict__ act, const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pairs,
         const int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles_p, const u16* __restrict__ W0,
-        const u16* __restrict__ W1, const float* __restrict__ topk_w, int top_k, void* __restrict__ out, int Kdim,
+        const u16* __restrict__ W1, int top_k, void* __restrict__ out, int Kdim,
         int Ndim, int n_nb, int act_rows, int ldk, int kparts) {
     __shared__ __attribute__((aligned(1024))) u16 lds[NTB * TELEMS + NWB * WELEMS];
 
@@ -369,13 +367,11 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(
     const int live = real <= 0 ? 0 : min(8, 2 * ((real + 31) / 32));
     const int nstages = Kdim / GK;
     const size_t orow0 = (size_t)(beg + m0);
-    const int32_t* pair_of_row = DENSE ? nullptr : sorted_pairs + beg + m0;
     if constexpr (MODE == 1 && DENSE) out = static_cast<float*>(out) + (size_t)kb * act_rows * Ndim;
     switch (live) {
 #define BEAM_GEMM_CASE(L)                                                                                     \
     case L:                                                                                                   \
-        gemm_run<MODE, L, PK>(lds, src, nstages, wave, lane, tok0, wrow, rows, orow0, c0, Ndim, pair_of_row,  \
-                              topk_w, out);                                                                   \
+        gemm_run<MODE, L, PK>(lds, src, nstages, wave, lane, tok0, wrow, rows, orow0, c0, Ndim, out);          \
         break;
         BEAM_GEMM_CASE(0) BEAM_GEMM_CASE(2) BEAM_GEMM_CASE(4) BEAM_GEMM_CASE(6) BEAM_GEMM_CASE(8)
 #undef BEAM_GEMM_CASE
@@ -447,7 +443,6 @@ template <int MODE, int LH>
 __device__ __forceinline__ void ws_run(u16* lds, __amdgpu_buffer_rsrc_t trs, const uint32_t (&toff)[ws_nt<LH>()],
                                        const __amdgpu_buffer_rsrc_t (&wrs)[2], int nstages, int wave, int lane,
                                        int rows, size_t orow0, const int (&chq)[2], int Ndim,
-                                       const int32_t* __restrict__ pair_of_row, const float* __restrict__ topk_w,
                                        void* __restrict__ out) {
     constexpr int NT = ws_nt<LH>();           // token loads per stage
     constexpr int NWL = 4;                    // weight loads per stage: 2 blocks x 2 k-halves
@@ -549,13 +544,12 @@ __device__ __forceinline__ void ws_run(u16* lds, __amdgpu_buffer_rsrc_t trs, con
             *reinterpret_cast<uint2*>(h + orow * Ndim + ch) = make_uint2(lo, hi);
         } else {
             float* y = reinterpret_cast<float*>(out);
-            const float wt = topk_w[pair_of_row[rr]];
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
                 const int ch = chq[q] + rsub;
                 if (ch >= Ndim) continue;
                 *reinterpret_cast<float4*>(y + orow * Ndim + ch) =
-                    make_float4(wt * acc[i][q][0], wt * acc[i][q][1], wt * acc[i][q][2], wt * acc[i][q][3]);
+                    make_float4(acc[i][q][0], acc[i][q][1], acc[i][q][2], acc[i][q][3]);
             }
         }
     }
@@ -564,7 +558,7 @@ __device__ __forceinline__ void ws_run(u16* lds, __amdgpu_buffer_rsrc_t trs, con
 template <int MODE, int LH>
 __device__ __forceinline__ void ws_item(u16* lds, const u16* __restrict__ act, uint32_t act_bytes,
                                         const int32_t* __restrict__ sorted_pairs, int top_k, int beg, int m0, int rows,
-                                        int e, int n0, const u16* W0, const u16* W1, const float* __restrict__ topk_w,
+                                        int e, int n0, const u16* W0, const u16* W1,
                                         void* __restrict__ out, int Kdim, int Ndim, int wave, int lane) {
     // token offsets: load i of this wave covers rows 8(8i + wave) .. +8 of the tile, lane row
     // + lane/8, global chunk (lane % 8) ^ (lane / 8); rows past the expert's segment repeat its last
@@ -599,8 +593,7 @@ __device__ __forceinline__ void ws_item(u16* lds, const u16* __restrict__ act, u
         const size_t blk = ((size_t)e * Ndim + min(ch, Ndim - 16)) / 16;
         wrs[q] = ws_rsrc(W + blk * (size_t)Kdim * 16, (uint32_t)Kdim * 32u);
     }
-    ws_run<MODE, LH>(lds, trs, toff, wrs, Kdim / WK, wave, lane, rows, (size_t)(beg + m0), chq, Ndim,
-                     sorted_pairs + beg + m0, topk_w, out);
+    ws_run<MODE, LH>(lds, trs, toff, wrs, Kdim / WK, wave, lane, rows, (size_t)(beg + m0), chq, Ndim, out);
 }
 
 // MODE 0: out = h [P, I] bf16 = bf16(silu(act . Wg^T) * (act . Wu^T)), act = x rows gathered
@@ -614,7 +607,7 @@ __global__ __launch_bounds__(64 * WNW, 1) void grouped_gemm_ws_kernel(
         const int32_t* __restrict__ sorted_pairs, const int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles_p,
         // no __restrict__: loads through restrict-qualified read-only pointers are free to move past
         // the fences that keep the weight and token loads in the order the waits count on
-        const u16* W0, const u16* W1, const float* __restrict__ topk_w, int top_k, void* __restrict__ out, int Kdim,
+        const u16* W0, const u16* W1, int top_k, void* __restrict__ out, int Kdim,
         int Ndim, int n_nb) {
     __shared__ __attribute__((aligned(1024))) u16 lds[WNB * WTB];
     const int n_items = *n_tiles_p * n_nb;
@@ -647,7 +640,7 @@ __global__ __launch_bounds__(64 * WNW, 1) void grouped_gemm_ws_kernel(
     switch (lh) {
 #define BEAM_WS_CASE(L)                                                                                         \
     case L:                                                                                                     \
-        ws_item<MODE, L>(lds, act, act_bytes, sorted_pairs, top_k, beg, m0, rows, e, n0, W0, W1, topk_w, out,  \
+        ws_item<MODE, L>(lds, act, act_bytes, sorted_pairs, top_k, beg, m0, rows, e, n0, W0, W1, out,          \
                          Kdim, Ndim, wave, lane);                                                               \
         break;
         BEAM_WS_CASE(2) BEAM_WS_CASE(4) BEAM_WS_CASE(6) BEAM_WS_CASE(8)
@@ -685,32 +678,32 @@ void launch_gemm_swiglu(const Shape& s, const void* x, const int32_t* offsets, c
     if (ws_supports(s, s.d, x_bytes)) {
         hipLaunchKernelGGL((grouped_gemm_ws_kernel<0>), dim3((unsigned)blocks), dim3(64 * WNW), 0, st, (const u16*)x,
                            (uint32_t)x_bytes, offsets, sorted_pairs, tiles, n_tiles, (const u16*)Wg, (const u16*)Wu,
-                           nullptr, s.K, h, s.d, s.I, n_nb);
+                           s.K, h, s.d, s.I, n_nb);
         return;
     }
 #define BEAM_GU(PK)                                                                                           \
     hipLaunchKernelGGL((grouped_gemm_kernel<0, false, PK>), dim3((unsigned)blocks), dim3(NT), 0, st,           \
                        (const u16*)x, offsets, sorted_pairs, tiles, n_tiles, (const u16*)Wg, (const u16*)Wu,  \
-                       nullptr, s.K, h, s.d, s.I, n_nb, (int)s.T, s.d, 1)
+                       s.K, h, s.d, s.I, n_nb, (int)s.T, s.d, 1)
     if (s.packed) BEAM_GU(true); else BEAM_GU(false);
 #undef BEAM_GU
 }
 
 void launch_gemm_down(const Shape& s, const void* h, const int32_t* offsets, const int32_t* sorted_pairs,
-                      const float* topk_w, const int32_t* tiles, int32_t* n_tiles, const void* Wd,
+                      const int32_t* tiles, int32_t* n_tiles, const void* Wd,
                       float* y_perm, hipStream_t st) {
     const int n_nb = (s.d + GN - 1) / GN;
     const int blocks = (max_items(s, n_nb) + 7) / 8 * 8;
     const uint64_t h_bytes = (uint64_t)s.T * s.K * s.I * 2;
     if (ws_supports(s, s.I, h_bytes)) {
         hipLaunchKernelGGL((grouped_gemm_ws_kernel<1>), dim3((unsigned)blocks), dim3(64 * WNW), 0, st, (const u16*)h,
-                           (uint32_t)h_bytes, offsets, sorted_pairs, tiles, n_tiles, (const u16*)Wd, nullptr, topk_w,
+                           (uint32_t)h_bytes, offsets, sorted_pairs, tiles, n_tiles, (const u16*)Wd, nullptr,
                            s.K, y_perm, s.I, s.d, n_nb);
         return;
     }
 #define BEAM_DN(PK)                                                                                           \
     hipLaunchKernelGGL((grouped_gemm_kernel<1, false, PK>), dim3((unsigned)blocks), dim3(NT), 0, st,           \
-                       (const u16*)h, offsets, sorted_pairs, tiles, n_tiles, (const u16*)Wd, nullptr, topk_w, \
+                       (const u16*)h, offsets, sorted_pairs, tiles, n_tiles, (const u16*)Wd, nullptr, \
                        s.K, y_perm, s.I, s.d, n_nb, (int)(s.T * s.K), s.I, 1)
     if (s.packed) BEAM_DN(true); else BEAM_DN(false);
 #undef BEAM_DN
@@ -724,7 +717,7 @@ void launch_dense_swiglu(int64_t T, int d, int I, bool packed, const void* x, co
     const int items = (int)((T + GM - 1) / GM) * n_nb;
 #define BEAM_DGU(PK)                                                                                          \
     hipLaunchKernelGGL((grouped_gemm_kernel<0, true, PK>), dim3((unsigned)((items + 7) / 8 * 8)), dim3(NT), 0, st, \
-                       (const u16*)x, nullptr, nullptr, nullptr, nullptr, (const u16*)Wg, (const u16*)Wu, nullptr, 1, \
+                       (const u16*)x, nullptr, nullptr, nullptr, nullptr, (const u16*)Wg, (const u16*)Wu, 1,       \
                        h, d, I, n_nb, (int)T, d, 1)
     if (packed) BEAM_DGU(true); else BEAM_DGU(false);
 #undef BEAM_DGU
@@ -735,7 +728,7 @@ void launch_dense_down(int64_t T, int d, int I, bool packed, const void* h, cons
     const int items = (int)((T + GM - 1) / GM) * n_nb;
 #define BEAM_DDN(PK)                                                                                          \
     hipLaunchKernelGGL((grouped_gemm_kernel<1, true, PK>), dim3((unsigned)((items + 7) / 8 * 8)), dim3(NT), 0, st, \
-                       (const u16*)h, nullptr, nullptr, nullptr, nullptr, (const u16*)Wd, nullptr, nullptr, 1, y, I, d, \
+                       (const u16*)h, nullptr, nullptr, nullptr, nullptr, (const u16*)Wd, nullptr, 1, y, I, d,          \
                        n_nb, (int)T, I, 1)
     if (packed) BEAM_DDN(true); else BEAM_DDN(false);
 #undef BEAM_DDN
@@ -748,7 +741,7 @@ void launch_gemm_router(const Shape& s, const void* x, const void* WrS, float* z
     const int n_nb = (Ndim + GN - 1) / GN;
     const int items = (int)((s.T + GM - 1) / GM) * n_nb * ks;
     hipLaunchKernelGGL((grouped_gemm_kernel<1, true, false>), dim3((unsigned)((items + 7) / 8 * 8)), dim3(NT), 0, st,
-                       (const u16*)x, nullptr, nullptr, nullptr, nullptr, (const u16*)WrS, nullptr, nullptr, 1, zp,
+                       (const u16*)x, nullptr, nullptr, nullptr, nullptr, (const u16*)WrS, nullptr, 1, zp,
                        s.d / ks, Ndim, n_nb, (int)s.T, s.d, ks);
 }
 

@@ -50,15 +50,14 @@ void launch_gemm_swiglu(const Shape& s, const void* x, const int32_t* offsets, c
                         const int32_t* tiles, int32_t* n_tiles, const void* Wg, const void* Wu, void* h,
                         hipStream_t st);
 void launch_gemm_down(const Shape& s, const void* h, const int32_t* offsets, const int32_t* sorted_pairs,
-                      const float* topk_w, const int32_t* tiles, int32_t* n_tiles, const void* Wd,
-                      float* y_perm, hipStream_t st);
+                      const int32_t* tiles, int32_t* n_tiles, const void* Wd, float* y_perm, hipStream_t st);
 void launch_swiglu(const Shape& s, const void* x, const int32_t* offsets, const int32_t* sorted_pairs,
                    const int32_t* tiles, int32_t* n_tiles, const void* Wg, const void* Wu, void* h,
                    hipStream_t st);
 void launch_down(const Shape& s, const void* h, const int32_t* offsets, const int32_t* sorted_pairs,
-                 const float* topk_w, const int32_t* tiles, int32_t* n_tiles, const void* Wd, float* y_perm,
-                 hipStream_t st);
-void launch_combine(const Shape& s, const float* y_perm, const int32_t* pair_rank, float* y, hipStream_t st);
+                 const int32_t* tiles, int32_t* n_tiles, const void* Wd, float* y_perm, hipStream_t st);
+void launch_combine(const Shape& s, const float* y_perm, const int32_t* pair_rank, const float* topk_w, float* y,
+                    hipStream_t st);
 
 // Weights [rows, K] -> the packed layout of beam_moe_pack_weights (rows % 16 == 0, K % 32 == 0).
 void launch_pack_stream(const void* W, void* P, int64_t rows, int K, hipStream_t st);
@@ -71,8 +70,8 @@ void launch_fp8_quantize(int64_t rows, int K, const void* w, void* q, void* s, h
 bool fp8_supports(const Shape& s);
 void launch_swiglu_fp8(const Shape& s, const void* x, const int32_t* offsets, const int32_t* sorted_pairs,
                        const void* Wg8, const void* Wu8, const void* sg, const void* su, void* h, hipStream_t st);
-void launch_down_fp8(const Shape& s, const void* h, const int32_t* offsets, const int32_t* sorted_pairs,
-                     const float* topk_w, const void* Wd8, const void* sd, float* y_perm, hipStream_t st);
+void launch_down_fp8(const Shape& s, const void* h, const int32_t* offsets, const void* Wd8, const void* sd,
+                     float* y_perm, hipStream_t st);
 
 // Dense SwiGLU MLP through the same GEMM (grouped_gemm.hip).
 bool dense_supports(int64_t T, int d, int I);
@@ -87,8 +86,9 @@ void launch_dense_down(int64_t T, int d, int I, bool packed, const void* h, cons
 
 // Post-MLP RMSNorm + depth-scaled residual (residual.hip); rows of up to kPostMaxD floats.
 constexpr int kPostMaxD = 16384;
-void launch_combine_post_residual(const Shape& s, const float* y_perm, const int32_t* pair_rank, const void* post_w,
-                                  int layer, const float* resid, float* resid_out, float* y, hipStream_t st);
+void launch_combine_post_residual(const Shape& s, const float* y_perm, const int32_t* pair_rank, const float* topk_w,
+                                  const void* post_w, int layer, const float* resid, float* resid_out, float* y,
+                                  hipStream_t st);
 void launch_post_residual(const Shape& s, const float* y, const void* post_w, int layer, const float* resid,
                           float* resid_out, hipStream_t st);
 

@@ -22,16 +22,24 @@ namespace {
 
 __device__ __forceinline__ float4 add4(float4 a, float4 b) { return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w); }
 
+// w * v rounded to FP32 on its own (never contracted with the add that follows into an FMA).
+__device__ __forceinline__ float4 mul4(float w, float4 v) {
+#pragma clang fp contract(off)
+    return make_float4(w * v.x, w * v.y, w * v.z, w * v.w);
+}
+
 // A float4 of Y_perm, which the combine reads once (non-temporal).
 __device__ __forceinline__ float4 ld4_once(const float* p) {
     const u32x4 r = ld_once(p);
     return make_float4(__uint_as_float(r.x), __uint_as_float(r.y), __uint_as_float(r.z), __uint_as_float(r.w));
 }
 
-// COMBINE: src is Y_perm [T*K, d] read through pair_rank; else src is y [T, d].
+// COMBINE: src is Y_perm [T*K, d] read through pair_rank, slot j weighted by topk_w[t, j] (each
+// product rounded to FP32 on its own, then added in slot order); else src is y [T, d].
 template <bool COMBINE, int kThreads>
 __global__ __launch_bounds__(kThreads) void post_residual_kernel(const float* __restrict__ src,
-                                                                 const int32_t* __restrict__ pair_rank, int K,
+                                                                 const int32_t* __restrict__ pair_rank,
+                                                                 const float* __restrict__ topk_w, int K,
                                                                  int d, const u16* __restrict__ w, float keep,
                                                                  float add, float eps,
                                                                  const float* resid, float* resid_out,
@@ -44,16 +52,20 @@ __global__ __launch_bounds__(kThreads) void post_residual_kernel(const float* __
     float4 v[kMaxV];
     if constexpr (COMBINE) {
         int rk[16];
+        float wt[16];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) rk[j] = j < K ? pair_rank[t * K + j] : 0;
+        for (int j = 0; j < 16; ++j) {
+            rk[j] = j < K ? pair_rank[t * K + j] : 0;
+            wt[j] = j < K ? topk_w[t * K + j] : 0.0f;
+        }
 #pragma unroll
         for (int i = 0; i < kMaxV; ++i) {
             const int q = tid + i * kThreads;
             if (q < nq) {
-                float4 acc = ld4_once(src + (size_t)rk[0] * d + 4 * q);
+                float4 acc = mul4(wt[0], ld4_once(src + (size_t)rk[0] * d + 4 * q));
 #pragma unroll
                 for (int j = 1; j < 16; ++j)
-                    if (j < K) acc = add4(acc, ld4_once(src + (size_t)rk[j] * d + 4 * q));
+                    if (j < K) acc = add4(acc, mul4(wt[j], ld4_once(src + (size_t)rk[j] * d + 4 * q)));
                 v[i] = acc;
             }
         }
@@ -108,17 +120,18 @@ constexpr int kSmallBatch = 1024;
 
 }  // namespace
 
-void launch_combine_post_residual(const Shape& s, const float* y_perm, const int32_t* pair_rank, const void* post_w,
-                                  int layer, const float* resid, float* resid_out, float* y, hipStream_t st) {
+void launch_combine_post_residual(const Shape& s, const float* y_perm, const int32_t* pair_rank, const float* topk_w,
+                                  const void* post_w, int layer, const float* resid, float* resid_out, float* y,
+                                  hipStream_t st) {
     float keep, add;
     residual_factors(layer, &keep, &add);
     const u16* w = static_cast<const u16*>(post_w);
     if (s.T < kSmallBatch)
         hipLaunchKernelGGL((post_residual_kernel<true, 1024>), dim3((unsigned)s.T), dim3(1024), 0, st, y_perm,
-                           pair_rank, s.K, s.d, w, keep, add, s.eps, resid, resid_out, y);
+                           pair_rank, topk_w, s.K, s.d, w, keep, add, s.eps, resid, resid_out, y);
     else
         hipLaunchKernelGGL((post_residual_kernel<true, 256>), dim3((unsigned)s.T), dim3(256), 0, st, y_perm,
-                           pair_rank, s.K, s.d, w, keep, add, s.eps, resid, resid_out, y);
+                           pair_rank, topk_w, s.K, s.d, w, keep, add, s.eps, resid, resid_out, y);
 }
 
 void launch_post_residual(const Shape& s, const float* y, const void* post_w, int layer, const float* resid,
@@ -128,10 +141,10 @@ void launch_post_residual(const Shape& s, const float* y, const void* post_w, in
     const u16* w = static_cast<const u16*>(post_w);
     if (s.T < kSmallBatch)
         hipLaunchKernelGGL((post_residual_kernel<false, 1024>), dim3((unsigned)s.T), dim3(1024), 0, st, y, nullptr,
-                           0, s.d, w, keep, add, s.eps, resid, resid_out, nullptr);
+                           nullptr, 0, s.d, w, keep, add, s.eps, resid, resid_out, nullptr);
     else
-        hipLaunchKernelGGL((post_residual_kernel<false, 256>), dim3((unsigned)s.T), dim3(256), 0, st, y, nullptr, 0,
-                           s.d, w, keep, add, s.eps, resid, resid_out, nullptr);
+        hipLaunchKernelGGL((post_residual_kernel<false, 256>), dim3((unsigned)s.T), dim3(256), 0, st, y, nullptr,
+                           nullptr, 0, s.d, w, keep, add, s.eps, resid, resid_out, nullptr);
 }
 
 }  // namespace beam
