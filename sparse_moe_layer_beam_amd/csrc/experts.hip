@@ -257,12 +257,10 @@ __global__ __launch_bounds__(256, kDnOcc) void down_stream_kernel(const u16* __r
     }
 }
 
-// y[t] = sum over slots j = 0..K-1, in that order, of y_perm[pair_rank[t*K + j]]; slots with
-// pair_rank -1 (an expert this call does not hold: expert-parallel share) add nothing, and a
-// row with no slot left is 0. grid: (T, ceil(d / 1024)); each thread owns one float4 of the row.
-// y[t] = sum over the slots j, in slot order, of topk_w[t, j] * y_perm[rank(t, j)] (each product
-// rounded to FP32 on its own: no contraction into FMA). A rank of -1 (a slot outside an
-// expert-parallel share) contributes nothing.
+// y[t] = sum over the slots j = 0..K-1, in that order, of topk_w[t, j] * y_perm[pair_rank[t*K + j]]
+// (each product rounded to FP32 on its own: no contraction into FMA). Slots with pair_rank -1
+// (an expert this call does not hold: expert-parallel share) add nothing, and a row with no slot
+// left is 0. grid: (T, ceil(d / 1024)); each thread owns one float4 of the row.
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y_perm,
                                                       const int32_t* __restrict__ pair_rank,
                                                       const float* __restrict__ topk_w, int K, int d,

@@ -1,6 +1,6 @@
 // Tiled grouped GEMM for batches with many tokens per expert (prefill): the gate/up
-// projection with SwiGLU fused in the epilogue, and the down projection with the routing
-// weight fused in the epilogue. BF16 MFMA (v_mfma_f32_16x16x32_bf16), FP32 accumulation.
+// projection with SwiGLU fused in the epilogue, and the down projection (the combine applies
+// the routing weights). BF16 MFMA (v_mfma_f32_16x16x32_bf16), FP32 accumulation.
 //
 // Method: Transformers "Beam" model page (Overview: sparse MoE item, FP32 SwiGLU note;
 // BeamConfig: moe_intermediate_size, hidden_act) and archdb "Beam-1.0-501B-A23B" fact
@@ -229,10 +229,10 @@ __device__ __forceinline__ int claim_item(int32_t* q, int x, int per_xcd, int n_
 
 // MODE 0: out = h [P, I] bf16 = bf16(silu(act . Wg^T) * (act . Wu^T)), act = x rows gathered
 //         through sorted_pairs (token = pair / top_k); W0 = Wg, W1 = Wu, both [E, Ndim, Kdim].
-// MODE 1: out = y_perm [P, d] fp32 = w_pair * (act . Wd^T), act = h rows in sorted order;
+// MODE 1: out = y_perm [P, d] fp32 = act . Wd^T, act = h rows in sorted order;
 //         W0 = Wd [E, Ndim, Kdim].
 // DENSE: one expert holding all act_rows tokens in order (the dense SwiGLU MLP, the router
-//         logits): no tile list, no gather, weight 1; MODE 1 then writes y [T, Ndim] directly.
+//         logits): no tile list, no gather; MODE 1 then writes y [T, Ndim] directly.
 //         k may be cut into kparts parts of Kdim (rows ldk long); part kb writes its partial
 //         product to out + kb * act_rows * Ndim. Its items all cost
 //         the same and map to blocks statically; the grouped GEMMs claim theirs (claim_item)
@@ -598,7 +598,7 @@ __device__ __forceinline__ void ws_item(u16* lds, const u16* __restrict__ act, u
 
 // MODE 0: out = h [P, I] bf16 = bf16(silu(act . Wg^T) * (act . Wu^T)), act = x rows gathered
 //         through sorted_pairs; W0 = Wg, W1 = Wu, packed [E*Ndim, Kdim].
-// MODE 1: out = y_perm [P, d] fp32 = w_pair * (act . Wd^T), act = h rows in sorted order; W0 = Wd.
+// MODE 1: out = y_perm [P, d] fp32 = act . Wd^T, act = h rows in sorted order; W0 = Wd.
 // act_bytes: the size of act (below 4 GiB: buffer offsets are 32-bit); Kdim a multiple of 512.
 // Work items and their claim as in grouped_gemm_kernel (the tile list of the dispatch).
 template <int MODE>
