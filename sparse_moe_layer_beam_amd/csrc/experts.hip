@@ -491,7 +491,7 @@ int dense_rb_dn(int d) { return d % (16 * 5) == 0 ? 5 : 4; }
 // with the same arithmetic, as the whole layer would.
 bool experts_tiled(const Shape& s) { return gemm_supports(s) && s.T * (int64_t)s.K > 16 * (int64_t)s.route_E; }
 
-int experts_tile_m(const Shape& s) { return experts_tiled(s) ? gemm_tile_m() : 16 * kMT; }
+int experts_tile_m(const Shape& s) { return experts_tiled(s) ? gemm_tile_m(s) : 16 * kMT; }
 
 void launch_swiglu(const Shape& s, const void* x, const int32_t* offsets, const int32_t* sorted_pairs,
                    const int32_t* tiles, int32_t* n_tiles, const void* Wg, const void* Wu, void* h,

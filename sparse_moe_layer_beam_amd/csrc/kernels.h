@@ -40,7 +40,7 @@ void launch_dispatch(const Shape& s, const int32_t* idx, int32_t* offsets, int32
 // Experts (experts.hip: path choice, streaming kernels, combine; grouped_gemm.hip: tiled GEMM)
 int experts_tile_m(const Shape& s);
 bool experts_tiled(const Shape& s);
-int gemm_tile_m();
+int gemm_tile_m(const Shape& s);
 // Router logits of large batches on the tiled GEMM (grouped_gemm.hip): zp[kb][t][pl*E + e]
 // over k part kb of ks, for the three planes pl of the split router weight.
 void launch_gemm_router(const Shape& s, const void* x, const void* WrS, float* zp, int ks, hipStream_t st);
