@@ -119,6 +119,9 @@ def test_forward_packed_against_oracle_mid():
 # d = 384, I = 512: the down pass streams weights (k = I) over n-blocks of 256 output channels, the
 # second of which runs past d (its waves read a clamped block and store nothing); gate/up (k = d)
 # stays on the LDS-staged GEMM
+# ws_mid_T1500: both expert GEMMs on the weight-streaming kernel, tiles of 320 tokens whose live
+# 16-token subtile counts (oracle routing) take every value 2, 4, .., 20; ws_d384_T800: gate/up on
+# the LDS-staged kernel (d not a multiple of 512), down weight-streaming on tiles of 256
 WS_CASES = {
     "ws_mid_T1500": recipes.Workload(42, "ws_mid_T1500", T=1500, d=512, E=64, n_group=8, topk_group=4, top_k=8,
                                      I=512, hot_experts=4, hot_bias=0.5),

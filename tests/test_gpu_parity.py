@@ -175,8 +175,9 @@ def test_forward_parity_random_shape(i):
     _check_every_token(_random_workload(i), "random_%d" % i)
 
 
-# rows per compared block of each expert's segment: every m-tile of the tiled GEMMs (a multiple of
-# this many rows, starting at the expert's first row) holds at least one compared token
+# rows per compared block of each expert's segment, each expert's last row compared too: every
+# m-tile of the tiled GEMMs holds a compared token, as a full tile (256 or 320 rows from the
+# expert's first row) spans a whole block and the expert's last tile holds its last row
 _COVER_BLOCK = {2: 64, 3: 64, 4: 128}
 
 
