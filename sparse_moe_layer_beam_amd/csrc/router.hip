@@ -16,44 +16,80 @@ namespace {
 // Pre-MLP RMSNorm, one 256-thread block per token. Done in FP64 (the pages ask for at
 // least FP32): the bf16 rounding of x is then a function of h and w alone, independent
 // of the reduction order, so every consumer of x sees the same bits.
-__device__ __forceinline__ void rmsnorm_row(const u16* __restrict__ h, const u16* __restrict__ w,
-                                            u16* __restrict__ x, int d, double eps, int64_t t) {
-    const u16* hr = h + t * d;
-    double ss = 0.0;
-    for (int c = threadIdx.x * 8; c < d; c += 256 * 8) {
-        uint4 v = *reinterpret_cast<const uint4*>(hr + c);
-        uint32_t p[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            double a = bf16_to_f32((u16)(p[i] & 0xffffu)), b = bf16_to_f32((u16)(p[i] >> 16));
-            ss += a * a;
-            ss += b * b;
-        }
-    }
-    ss = wave_sum_f64(ss);
-    __shared__ double part[4];
-    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
-    __syncthreads();
-    ss = part[0] + part[1] + part[2] + part[3];
-    const double r = 1.0 / sqrt(ss / (double)d + eps);
-    for (int c = threadIdx.x * 8; c < d; c += 256 * 8) {
-        uint4 v = *reinterpret_cast<const uint4*>(hr + c);
-        uint4 g = *reinterpret_cast<const uint4*>(w + c);
-        uint32_t p[4] = {v.x, v.y, v.z, v.w}, q[4] = {g.x, g.y, g.z, g.w}, o[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            double a0 = bf16_to_f32((u16)(p[i] & 0xffffu)), a1 = bf16_to_f32((u16)(p[i] >> 16));
-            double w0 = bf16_to_f32((u16)(q[i] & 0xffffu)), w1 = bf16_to_f32((u16)(q[i] >> 16));
-            u16 lo = f64_to_bf16((a0 * r) * w0), hi = f64_to_bf16((a1 * r) * w1);
-            o[i] = (uint32_t)lo | ((uint32_t)hi << 16);
-        }
-        *reinterpret_cast<uint4*>(x + t * d + c) = make_uint4(o[0], o[1], o[2], o[3]);
-    }
+// bf16((a * r) * w) as the FP64 products round it (f64_to_bf16), mostly without FP64: the FP32
+// product p carries three roundings (r to FP32, then two products), so it lies within 3.0002 FP32
+// ulps of the FP64 one, and when p is at least 8 ulps from a bf16 rounding midpoint both round to
+// the same bf16. The rest (near a midpoint, zero or subnormal exponent field, inf) take FP64.
+__device__ __forceinline__ u16 norm_to_bf16(u16 ab, u16 wb, float r32, double r) {
+    const float a = bf16_to_f32(ab), w = bf16_to_f32(wb);
+    const float p = (a * r32) * w;
+    const uint32_t u = __float_as_uint(p);
+    const uint32_t ex = (u >> 23) & 0xffu;
+    const int dist = (int)(u & 0xffffu) - 0x8000;
+    if (ex != 0u && ex != 0xffu && (dist >= 8 || dist <= -8)) return (u16)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+    return f64_to_bf16(((double)a * r) * (double)w);
 }
 
+// Sum of the squares of the 8 bf16 values in v, in FP64 (exact products, rounded sums).
+__device__ __forceinline__ double sumsq8(uint4 v, double ss) {
+    const uint32_t p[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const double a = bf16_to_f32((u16)(p[i] & 0xffffu)), b = bf16_to_f32((u16)(p[i] >> 16));
+        ss += a * a;
+        ss += b * b;
+    }
+    return ss;
+}
+
+__device__ __forceinline__ uint4 norm8(uint4 v, uint4 g, float r32, double r) {
+    const uint32_t p[4] = {v.x, v.y, v.z, v.w}, q[4] = {g.x, g.y, g.z, g.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const u16 lo = norm_to_bf16((u16)(p[i] & 0xffffu), (u16)(q[i] & 0xffffu), r32, r);
+        const u16 hi = norm_to_bf16((u16)(p[i] >> 16), (u16)(q[i] >> 16), r32, r);
+        o[i] = (uint32_t)lo | ((uint32_t)hi << 16);
+    }
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+constexpr int kNormChunks = 16;    // 8-value chunks per lane loaded together for the sum of squares
+
+// x[t] = bf16((h[t] * r) * w), r = 1 / sqrt(mean(h[t]^2) + eps), the sum of squares and r in FP64:
+// one wave per token row. The first pass issues all its loads of a row (up to 64 * 8 * kNormChunks
+// values at a time) before it adds; the second reads the row again, from cache.
+__device__ __forceinline__ void rmsnorm_row(const u16* __restrict__ h, const u16* __restrict__ w,
+                                            u16* __restrict__ x, int d, double eps, int64_t t) {
+    const int lane = threadIdx.x & 63;
+    const u16* hr = h + t * d;
+    u16* xr = x + t * d;
+    double ss = 0.0;
+    for (int c0 = 0; c0 < d; c0 += 64 * 8 * kNormChunks) {
+        uint4 v[kNormChunks];
+#pragma unroll
+        for (int i = 0; i < kNormChunks; ++i) {
+            const int c = c0 + (lane + 64 * i) * 8;
+            v[i] = c < d ? *reinterpret_cast<const uint4*>(hr + c) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < kNormChunks; ++i) ss = sumsq8(v[i], ss);
+    }
+    ss = wave_sum_f64(ss);
+    const double r = 1.0 / sqrt(ss / (double)d + eps);
+    const float r32 = (float)r;
+#pragma unroll 2
+    for (int c = lane * 8; c < d; c += 64 * 8)
+        *reinterpret_cast<uint4*>(xr + c) =
+            norm8(*reinterpret_cast<const uint4*>(hr + c), *reinterpret_cast<const uint4*>(w + c), r32, r);
+}
+
+constexpr int kNormRows = 4;    // token rows per 256-thread block, one per wave
+
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const u16* __restrict__ h, const u16* __restrict__ w,
-                                                      u16* __restrict__ x, int d, double eps) {
-    rmsnorm_row(h, w, x, d, eps, blockIdx.x);
+                                                      u16* __restrict__ x, int d, double eps, int64_t T) {
+    const int64_t t = (int64_t)blockIdx.x * kNormRows + (threadIdx.x >> 6);
+    if (t < T) rmsnorm_row(h, w, x, d, eps, t);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -338,18 +374,19 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float* __restri
 }
 
 // The two passes that precede the router product when the layer opens with the pre-MLP
-// RMSNorm, in one launch: blocks [0, T) norm one token each (x = bf16(h * r * w), the x the
-// router and the experts read), blocks [T, T + (d/64)(E/64)) split one 64 x 64 tile of Wr.
+// RMSNorm, in one launch: blocks [0, nbn) norm kNormRows tokens each (x = bf16(h * r * w), the x
+// the router and the experts read), blocks [nbn, nbn + (d/64)(E/64)) split one 64 x 64 tile of Wr.
 __global__ __launch_bounds__(256) void router_prep_kernel(const u16* __restrict__ h, const u16* __restrict__ w,
                                                           u16* __restrict__ x, double eps, int64_t T,
                                                           const float* __restrict__ Wr, u16* __restrict__ WrS,
                                                           int d, int E) {
-    const int64_t b = blockIdx.x;
-    if (b < T) {
-        rmsnorm_row(h, w, x, d, eps, b);
+    const int64_t b = blockIdx.x, nbn = (T + kNormRows - 1) / kNormRows;
+    if (b < nbn) {
+        const int64_t t = b * kNormRows + (threadIdx.x >> 6);
+        if (t < T) rmsnorm_row(h, w, x, d, eps, t);
         return;
     }
-    const int tile = (int)(b - T), nk = d / 64;
+    const int tile = (int)(b - nbn), nk = d / 64;
     split_tile(Wr, WrS, d, E, (tile % nk) * 64, (tile / nk) * 64);
 }
 
@@ -482,8 +519,8 @@ __global__ __launch_bounds__(256, 2) void router_mfma_kernel(const u16* __restri
 }  // namespace
 
 void launch_rmsnorm(const Shape& s, const void* h, const void* w, void* x_out, hipStream_t st) {
-    hipLaunchKernelGGL(rmsnorm_kernel, dim3((unsigned)s.T), dim3(256), 0, st, (const u16*)h, (const u16*)w,
-                       (u16*)x_out, s.d, (double)s.eps);
+    hipLaunchKernelGGL(rmsnorm_kernel, dim3((unsigned)((s.T + kNormRows - 1) / kNormRows)), dim3(256), 0, st,
+                       (const u16*)h, (const u16*)w, (u16*)x_out, s.d, (double)s.eps, s.T);
 }
 
 bool router_uses_mfma(const Shape& s) { return (s.E == 128 || s.E == 256) && s.d % 64 == 0; }
@@ -551,7 +588,7 @@ void launch_router(const Shape& s, const void* h, const void* norm_w, void* x_no
     // when there is one, in the same launch)
     const void* x = norm_w ? x_normed : h;
     if (split && norm_w) {
-        const unsigned nb = (unsigned)(s.T + (int64_t)(s.d / 64) * (s.E / 64));
+        const unsigned nb = (unsigned)((s.T + kNormRows - 1) / kNormRows + (int64_t)(s.d / 64) * (s.E / 64));
         hipLaunchKernelGGL(router_prep_kernel, dim3(nb), dim3(256), 0, st, (const u16*)h, (const u16*)norm_w,
                            (u16*)x_normed, (double)s.eps, s.T, Wr, (u16*)wrs, s.d, s.E);
     } else if (split) {
