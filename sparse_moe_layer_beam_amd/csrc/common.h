@@ -45,7 +45,12 @@ __device__ __forceinline__ uint32_t f32_order_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+// silu(g) * u in FP32 with the hardware exponential and reciprocal (about 1 ulp each): against
+// the IEEE division and the library expf, the prefill gate/up GEMM at T=8192 ran 3.54-3.57 ->
+// 3.50-3.51 ms on MI355X. g -> -inf gives -0 (exp overflows, the reciprocal is 0), g -> +inf g * u.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+    return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
 
 template <typename T>
 __device__ __forceinline__ T wave_shfl_xor(T v, int m) { return __shfl_xor(v, m, kWave); }
