@@ -22,6 +22,8 @@
 // Also here: the packing kernel itself, and the dense SwiGLU MLP for decode-sized batches
 // (Transformers "Beam" page, Overview: the first 3 layers use a dense MLP), which streams its
 // weights the same way against packed 16-token tiles.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -316,8 +318,8 @@ __global__ __launch_bounds__(256) void pack_stream_kernel(const u16* __restrict_
 // All T tokens are one expert; every weight byte must serve all of them in one pass. The
 // tokens go to packed 16-token tiles first (four tiles, padded with the last token), so each
 // wave's token fragments are contiguous kilobytes like its weight fragments. In both kernels
-// the 4 waves of a block stream the same weight rows over four consecutive parts of k against
-// the four tiles, and their sums meet in LDS, added in part order. Measured on MI355X at
+// the waves that stream the same weight rows take four consecutive parts of k against the four
+// tiles, and their sums meet in LDS, added in part order. Measured on MI355X at
 // T = 64, d = 5120, I = 20480 (packed weights): 0.142-0.146 ms with each token fragment feeding four
 // weight fragments (two gate and two up 16-row blocks; four 16-row blocks of Wd), a 3-deep ring
 // and two blocks per CU, against 0.158 ms with two weight fragments per token fragment (1:1 -> 2:1
@@ -325,19 +327,19 @@ __global__ __launch_bounds__(256) void pack_stream_kernel(const u16* __restrict_
 // eight weight fragments (one wave per SIMD); 0.190 ms with every k part written out and added by a
 // second kernel. Results are bitwise the same in every form (the k order of each sum is unchanged).
 // With the down pass in one round (dense_rb_dn): 0.133 ms; gate/up 87 us for 419 MB, down 41 us,
-// token packing 6 us, the k-part sum 5 us. Tried on the gate/up pass without gain: ring depth 4
+// token packing 6 us, the k-part sum 5 us; with gate/up in one round too (dense_gu_stream8_kernel)
+// 0.1245 ms. Tried on the gate/up pass without gain (before that): ring depth 4
 // and 5 (0.140, 0.150 ms), each block starting its k walk at a different step (0.133), the
 // unit's weight blocks read as if interleaved per k step (0.133), and the launch's last partial
 // round split into k quarters added by the last block to finish (-1 us, not kept). A copy that
-// skips the token fragment reloads runs 0.115 ms: the token reads, not the weight stream's
-// DRAM pattern, hold this pass at ~4.8 TB/s. Reading x rows directly (16 rows x 64 B per
+// skipped the token fragment reloads ran 0.115 ms (its shorter blocks also shrank the second
+// round). Reading x rows directly (16 rows x 64 B per
 // fragment, no packing launch) ran 0.163 ms against 0.136; the k-part sum folded into the down
 // pass (the last block of a column group adds the parts) 0.1375 against 0.1355.
 constexpr int kDT = 4;                   // token tiles (64 tokens)
 constexpr int kDD = 3;                   // ring depth of the dense streams
 constexpr int kDenseKsDN = 8;            // most k parts of the down pass across blocks
-constexpr int kDenseCG = 2;              // gate/up: 16-channel groups per block (2*kDenseCG weight rows per token fragment)
-constexpr int kDenseOcc = 2;             // blocks of 4 waves per CU the registers must allow
+constexpr int kDenseOcc = 2;             // down: blocks of 4 waves per CU the registers must allow
 
 // Adds the other waves' accumulators to wave 0's, in wave order. Returns true in wave 0.
 template <int NA>
@@ -363,47 +365,76 @@ __device__ __forceinline__ bool dense_reduce(f32x4 (&red)[kWavesPerBlock - 1][kD
 }
 
 // hp = bf16(silu(x . Wg[n]) * (x . Wu[n])) for all 64 token slots, written as packed token tiles
-// for the down pass. grid: I / (16 CG); block: 4 waves, wave w streaming the gate and up rows of
-// the block's CG groups of 16 channels over k part w of 4: each token fragment feeds 2 CG weight
-// fragments.
-template <bool PK, int CG>
-__global__ __launch_bounds__(256, kDenseOcc) void dense_gu_stream_kernel(const u16* __restrict__ xp,
-                                                                      const u16* __restrict__ Wg,
-                                                                      const u16* __restrict__ Wu,
-                                                                      u16* __restrict__ hp, int d, int I) {
-    __shared__ f32x4 red[kWavesPerBlock - 1][kDT][2 * CG][64];
+// for the down pass, with one block of 8 waves per CU so that the launch is one round of the CUs:
+// wave w streams RBW 16-row blocks over k quarter w % 4 against the four token tiles, the gate rows
+// of the block's RBW 16-channel groups (w < 4) or their up rows (w >= 4); the quarters of each are
+// added in quarter order through LDS, then the up sums meet the gate sums for the SwiGLU.
+// grid: ceil(I / (16 RBW)). At I = 20480 (1280 groups) RBW = 5 gives 256 blocks; the form before,
+// 640 blocks of 4 waves (two 16-channel groups each) at two blocks per CU, ran its last 128 blocks
+// as a second round on half the CUs: T=64 layer 0.1344 -> 0.1245 ms on MI355X, bitwise the same y.
+template <bool PK, int RBW>
+__global__ __launch_bounds__(512, 1) void dense_gu_stream8_kernel(const u16* __restrict__ xp,
+                                                                  const u16* __restrict__ Wg,
+                                                                  const u16* __restrict__ Wu,
+                                                                  u16* __restrict__ hp, int d, int I) {
+    __shared__ f32x4 red[2][kWavesPerBlock - 1][kDT][RBW][64];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int n0 = blockIdx.x * 16 * CG;
-    const int kl = d / kWavesPerBlock, k0 = wave * kl;
-    const u16* a[2 * CG];
+    const int kq = wave & 3, half = wave >> 2;
+    const int ngr = I / 16, g0 = blockIdx.x * RBW;
+    const int kl = d / kWavesPerBlock, k0 = kq * kl;
+    const u16* const W = half ? Wu : Wg;
+    const u16* a[RBW];
 #pragma unroll
-    for (int g = 0; g < CG; ++g) {
-        const int ng = n0 + 16 * g;
-        const size_t wo = PK ? ((size_t)ng / 16 * (d / 32) * 64 + lane) * 8 + (size_t)k0 * 16
-                             : (size_t)(ng + (lane & 15)) * d + (lane >> 4) * 8 + k0;
-        a[g] = Wg + wo;
-        a[CG + g] = Wu + wo;
+    for (int r = 0; r < RBW; ++r) {
+        const int ng = min(g0 + r, ngr - 1) * 16;       // groups past I repeat the last (not stored)
+        a[r] = W + (PK ? ((size_t)ng / 16 * (d / 32) * 64 + lane) * 8 + (size_t)k0 * 16
+                       : (size_t)(ng + (lane & 15)) * d + (lane >> 4) * 8 + k0);
     }
     const u16* xb[kDT];
 #pragma unroll
     for (int m = 0; m < kDT; ++m) xb[m] = xp + ((size_t)m * (d / 32) * 64 + lane) * 8 + (size_t)k0 * 16;
-    f32x4 acc[kDT][2 * CG];
+    f32x4 acc[kDT][RBW];
 #pragma unroll
     for (int m = 0; m < kDT; ++m)
 #pragma unroll
-        for (int q = 0; q < 2 * CG; ++q) acc[m][q] = f32x4{0, 0, 0, 0};
-    stream_core<2 * CG, kDT, kDD, PK, true>(a, xb, kl, acc);
-    if (!dense_reduce<2 * CG>(red, wave, lane, acc)) return;
-    // lane holds channels c .. c+3 (c = n0 + 16 g + 4 (lane / 16)) of token slot 16 m + lane % 16; in
-    // the packed tiles they are elements c % 8 .. +3 of the 8-element chunk of k-step c / 32,
-    // lane (lane % 16) + 16 ((c % 32) / 8)
+        for (int r = 0; r < RBW; ++r) acc[m][r] = f32x4{0, 0, 0, 0};
+    stream_core<RBW, kDT, kDD, PK, true>(a, xb, kl, acc);
+    if (kq != 0)
 #pragma unroll
-    for (int g = 0; g < CG; ++g) {
-        const int c = n0 + 16 * g + 4 * (lane >> 4);
+        for (int m = 0; m < kDT; ++m)
+#pragma unroll
+            for (int r = 0; r < RBW; ++r) red[half][kq - 1][m][r][lane] = acc[m][r];
+    __syncthreads();
+    if (kq == 0)
+#pragma unroll
+        for (int j = 0; j < kWavesPerBlock - 1; ++j)
+#pragma unroll
+            for (int m = 0; m < kDT; ++m)
+#pragma unroll
+                for (int r = 0; r < RBW; ++r) {
+                    const f32x4 v = red[half][j][m][r][lane];
+                    acc[m][r] = f32x4{acc[m][r][0] + v[0], acc[m][r][1] + v[1], acc[m][r][2] + v[2],
+                                      acc[m][r][3] + v[3]};
+                }
+    __syncthreads();
+    if (kq == 0 && half == 1)
+#pragma unroll
+        for (int m = 0; m < kDT; ++m)
+#pragma unroll
+            for (int r = 0; r < RBW; ++r) red[0][0][m][r][lane] = acc[m][r];
+    __syncthreads();
+    if (kq != 0 || half != 0) return;
+    // lane holds channels c .. c+3 (c = 16 g + 4 (lane / 16)) of token slot 16 m + lane % 16; in the
+    // packed tiles they are elements c % 8 .. +3 of the 8-element chunk of k-step c / 32, lane
+    // (lane % 16) + 16 ((c % 32) / 8)
+#pragma unroll
+    for (int r = 0; r < RBW; ++r) {
+        if (g0 + r >= ngr) break;
+        const int c = (g0 + r) * 16 + 4 * (lane >> 4);
         const int pl = (lane & 15) + 16 * ((c & 31) >> 3);
 #pragma unroll
         for (int m = 0; m < kDT; ++m) {
-            const f32x4 gv = acc[m][g], uv = acc[m][CG + g];
+            const f32x4 gv = acc[m][r], uv = red[0][0][m][r][lane];
             const uint32_t lo = (uint32_t)f32_to_bf16(silu_mul(gv[0], uv[0])) |
                                 ((uint32_t)f32_to_bf16(silu_mul(gv[1], uv[1])) << 16);
             const uint32_t hi = (uint32_t)f32_to_bf16(silu_mul(gv[2], uv[2])) |
@@ -549,7 +580,6 @@ void launch_pack_stream(const void* W, void* P, int64_t rows, int K, hipStream_t
 
 // every wave of both passes streams a whole number of 32-wide k-steps: d, I multiples of 128
 bool dense_stream_supports(int64_t T, int d, int I) {
-    static_assert(128 % (16 * kDenseCG) == 0, "whole row blocks per block");
     return T >= 1 && T <= 16 * kDT && d % 128 == 0 && I % 128 == 0;
 }
 
@@ -574,13 +604,24 @@ void launch_dense_stream(int64_t T, int d, int I, bool packed, const void* x, co
     const int64_t xchunks = (int64_t)kDT * (d / 32) * 64;
     hipLaunchKernelGGL(pack_stream_kernel, dim3((unsigned)((xchunks + 255) / 256)), dim3(256), 0, st, (const u16*)x,
                        xp, (int64_t)tp, T, d);
-    const dim3 ggu((unsigned)(I / (16 * kDenseCG))), gdn((unsigned)(d / (16 * rb)), (unsigned)ks_dn);
-    if (packed)
-        hipLaunchKernelGGL((dense_gu_stream_kernel<true, kDenseCG>), ggu, dim3(256), 0, st, xp, (const u16*)Wg,
-                           (const u16*)Wu, hp, d, I);
-    else
-        hipLaunchKernelGGL((dense_gu_stream_kernel<false, kDenseCG>), ggu, dim3(256), 0, st, xp, (const u16*)Wg,
-                           (const u16*)Wu, hp, d, I);
+    const dim3 gdn((unsigned)(d / (16 * rb)), (unsigned)ks_dn);
+    // 16-channel groups per gate/up block: the fewest that cover I in one block per CU, at most 5
+    const int ngr = I / 16, rbw = std::min(5, std::max(1, (ngr + 255) / 256));
+    const dim3 ggu((unsigned)((ngr + rbw - 1) / rbw));
+#define BEAM_DGU8(PK, R)                                                                                       \
+    hipLaunchKernelGGL((dense_gu_stream8_kernel<PK, R>), ggu, dim3(512), 0, st, xp, (const u16*)Wg,          \
+                       (const u16*)Wu, hp, d, I)
+#define BEAM_DGU8_R(PK)                                                                                        \
+    switch (rbw) {                                                                                             \
+        case 1: BEAM_DGU8(PK, 1); break;                                                                       \
+        case 2: BEAM_DGU8(PK, 2); break;                                                                       \
+        case 3: BEAM_DGU8(PK, 3); break;                                                                       \
+        case 4: BEAM_DGU8(PK, 4); break;                                                                       \
+        default: BEAM_DGU8(PK, 5); break;                                                                      \
+    }
+    if (packed) { BEAM_DGU8_R(true) } else { BEAM_DGU8_R(false) }
+#undef BEAM_DGU8_R
+#undef BEAM_DGU8
 #define BEAM_DDN(PK, RB)                                                                                       \
     hipLaunchKernelGGL((dense_dn_stream_kernel<PK, RB>), gdn, dim3(256), 0, st, hp, (const u16*)Wd, part_dn, d, I)
     if (rb == 5) {
