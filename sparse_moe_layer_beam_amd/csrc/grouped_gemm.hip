@@ -381,7 +381,7 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(
 // ---- packed weights: weights streamed into registers, tokens through LDS --------------------
 //
 // The same kind of work items as grouped_gemm_kernel (an expert's m-tile of up to 320 tokens, or
-// 256 when the other expert GEMM runs grouped_gemm_kernel, x an n-block
+// 256 when the other expert GEMM runs grouped_gemm_kernel, or the dense MLP's m-tiles, x an n-block
 // of 256 weight rows), the same arithmetic (16x16x32 bf16 MFMAs over k in order into FP32
 // accumulators, the same epilogues), organised for packed weights:
 //  * eight waves, two per SIMD: wave w owns two 16-row weight blocks (gate/up: the gate rows and
@@ -440,12 +440,13 @@ constexpr int ws_rw() {
 }
 
 // K loop and epilogue of one wave of a tile with LH live 16-token subtiles (even, 2..20).
-template <int MODE, int LH>
-__device__ __forceinline__ void ws_run(u16* lds, __amdgpu_buffer_rsrc_t trs, const uint32_t (&toff)[ws_nt<LH>()],
+template <int MODE, int LH, int NTT>
+__device__ __forceinline__ void ws_run(u16* lds, __amdgpu_buffer_rsrc_t trs, const uint32_t (&toff)[NTT],
                                        const __amdgpu_buffer_rsrc_t (&wrs)[2], int nstages, int wave, int lane,
                                        int rows, size_t orow0, const int (&chq)[2], int Ndim,
                                        void* __restrict__ out) {
     constexpr int NT = ws_nt<LH>();           // token loads per stage
+    static_assert(NTT == NT, "one token offset per token load");
     constexpr int NWL = 4;                    // weight loads per stage: 2 blocks x 2 k-halves
     constexpr int WRW = ws_rw<LH>();
     // loads issued after a stage's token loads, up to that stage: the weight refill issued with
@@ -570,7 +571,8 @@ __device__ __forceinline__ void ws_item(u16* lds, const u16* __restrict__ act, u
     for (int i = 0; i < NT; ++i) {
         const int m = m0 + min(8 * (WNW * i + wave) + (lane >> 3), rows - 1);
         uint32_t tr;
-        if constexpr (MODE == 0) tr = (uint32_t)(sorted_pairs[beg + m] / top_k);
+        // gate/up gathers the tokens of its pairs; the dense MLP (no sorted_pairs) takes them in order
+        if (MODE == 0 && sorted_pairs) tr = (uint32_t)(sorted_pairs[beg + m] / top_k);
         else tr = (uint32_t)(beg + m);
         toff[i] = (tr * (uint32_t)Kdim + 8u * chunk) * 2u;
     }
@@ -602,27 +604,44 @@ __device__ __forceinline__ void ws_item(u16* lds, const u16* __restrict__ act, u
 // MODE 1: out = y_perm [P, d] fp32 = act . Wd^T, act = h rows in sorted order; W0 = Wd.
 // act_bytes: the size of act (below 4 GiB: buffer offsets are 32-bit); Kdim a multiple of 512.
 // Work items and their claim as in grouped_gemm_kernel (the tile list of the dispatch).
-template <int MODE>
+// DENSE: one expert holding all act_rows tokens in order (the dense SwiGLU MLP): items from
+// act_rows directly, statically mapped XCD by XCD, no gather; MODE 1 then writes y [T, Ndim].
+template <int MODE, bool DENSE>
 __global__ __launch_bounds__(64 * WNW, 1) void grouped_gemm_ws_kernel(
         const u16* __restrict__ act, uint32_t act_bytes, const int32_t* __restrict__ offsets,
         const int32_t* __restrict__ sorted_pairs, const int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles_p,
         // no __restrict__: loads through restrict-qualified read-only pointers are free to move past
         // the fences that keep the weight and token loads in the order the waits count on
         const u16* W0, const u16* W1, int top_k, void* __restrict__ out, int Kdim,
-        int Ndim, int n_nb, int tile_m) {
+        int Ndim, int n_nb, int tile_m, int act_rows) {
     __shared__ __attribute__((aligned(1024))) u16 lds[WNB * WTB];
-    const int n_items = *n_tiles_p * n_nb;
-    const int per_xcd = (n_items + 7) / 8;
-    if ((int)blockIdx.x >= n_items + n_items / 4 + 64) return;
-    const int item = claim_item(n_tiles_p + 1 + 8 * MODE, blockIdx.x & 7, per_xcd, n_items, lds);
-    if (item < 0) return;
-    const int j = item / n_nb;
-    const int e = tiles[4 * j];
-    const int first = tiles[4 * j + 2];
-    const int cnt = tiles[4 * j + 3];
-    const int local = item - first * n_nb;
-    const int beg = offsets[e];
-    const int n_e = offsets[e + 1] - beg;
+    int e, beg, n_e, cnt, local;
+    if constexpr (DENSE) {
+        const int n_mt = (act_rows + tile_m - 1) / tile_m;
+        const int n_items = n_mt * n_nb;
+        const int per_xcd = (n_items + 7) / 8;
+        const int slot = blockIdx.x >> 3;
+        if (slot >= per_xcd) return;
+        local = (blockIdx.x & 7) * per_xcd + slot;
+        if (local >= n_items) return;
+        e = 0;
+        beg = 0;
+        n_e = act_rows;
+        cnt = n_mt;
+    } else {
+        const int n_items = *n_tiles_p * n_nb;
+        const int per_xcd = (n_items + 7) / 8;
+        if ((int)blockIdx.x >= n_items + n_items / 4 + 64) return;
+        const int item = claim_item(n_tiles_p + 1 + 8 * MODE, blockIdx.x & 7, per_xcd, n_items, lds);
+        if (item < 0) return;
+        const int j = item / n_nb;
+        e = tiles[4 * j];
+        const int first = tiles[4 * j + 2];
+        cnt = tiles[4 * j + 3];
+        local = item - first * n_nb;
+        beg = offsets[e];
+        n_e = offsets[e + 1] - beg;
+    }
     // the expert's n_nb x cnt items in groups of four n-blocks, m-tile-major inside a group (on
     // MI355X, against groups of two: T=8192 layer 6.32 -> 6.15 ms, T=32768 19.9 -> 19.75; eight: 6.26)
     constexpr int GW = 4;
@@ -688,9 +707,9 @@ void launch_gemm_swiglu(const Shape& s, const void* x, const int32_t* offsets, c
     const int blocks = (max_items(s, n_nb, tile_m) + 7) / 8 * 8;
     const uint64_t x_bytes = (uint64_t)s.T * s.d * 2;
     if (ws_supports(s, s.d, x_bytes)) {
-        hipLaunchKernelGGL((grouped_gemm_ws_kernel<0>), dim3((unsigned)blocks), dim3(64 * WNW), 0, st, (const u16*)x,
-                           (uint32_t)x_bytes, offsets, sorted_pairs, tiles, n_tiles, (const u16*)Wg, (const u16*)Wu,
-                           s.K, h, s.d, s.I, n_nb, tile_m);
+        hipLaunchKernelGGL((grouped_gemm_ws_kernel<0, false>), dim3((unsigned)blocks), dim3(64 * WNW), 0, st,
+                           (const u16*)x, (uint32_t)x_bytes, offsets, sorted_pairs, tiles, n_tiles, (const u16*)Wg,
+                           (const u16*)Wu, s.K, h, s.d, s.I, n_nb, tile_m, 0);
         return;
     }
 #define BEAM_GU(PK)                                                                                           \
@@ -709,9 +728,9 @@ void launch_gemm_down(const Shape& s, const void* h, const int32_t* offsets, con
     const int blocks = (max_items(s, n_nb, tile_m) + 7) / 8 * 8;
     const uint64_t h_bytes = (uint64_t)s.T * s.K * s.I * 2;
     if (ws_supports(s, s.I, h_bytes)) {
-        hipLaunchKernelGGL((grouped_gemm_ws_kernel<1>), dim3((unsigned)blocks), dim3(64 * WNW), 0, st, (const u16*)h,
-                           (uint32_t)h_bytes, offsets, sorted_pairs, tiles, n_tiles, (const u16*)Wd, nullptr,
-                           s.K, y_perm, s.I, s.d, n_nb, tile_m);
+        hipLaunchKernelGGL((grouped_gemm_ws_kernel<1, false>), dim3((unsigned)blocks), dim3(64 * WNW), 0, st,
+                           (const u16*)h, (uint32_t)h_bytes, offsets, sorted_pairs, tiles, n_tiles, (const u16*)Wd,
+                           nullptr, s.K, y_perm, s.I, s.d, n_nb, tile_m, 0);
         return;
     }
 #define BEAM_DN(PK)                                                                                           \
@@ -727,6 +746,14 @@ void launch_gemm_down(const Shape& s, const void* h, const int32_t* offsets, con
 void launch_dense_swiglu(int64_t T, int d, int I, bool packed, const void* x, const void* Wg, const void* Wu, void* h,
                          hipStream_t st) {
     const int n_nb = (I + GN / 2 - 1) / (GN / 2);
+    const uint64_t x_bytes = (uint64_t)T * d * 2;
+    if (packed && d % (WK * WUN) == 0 && x_bytes < ((uint64_t)1 << 32)) {
+        const int ws_items = (int)((T + WM - 1) / WM) * n_nb;
+        hipLaunchKernelGGL((grouped_gemm_ws_kernel<0, true>), dim3((unsigned)((ws_items + 7) / 8 * 8)),
+                           dim3(64 * WNW), 0, st, (const u16*)x, (uint32_t)x_bytes, nullptr, nullptr, nullptr,
+                           nullptr, (const u16*)Wg, (const u16*)Wu, 1, h, d, I, n_nb, WM, (int)T);
+        return;
+    }
     const int items = (int)((T + GM - 1) / GM) * n_nb;
 #define BEAM_DGU(PK)                                                                                          \
     hipLaunchKernelGGL((grouped_gemm_kernel<0, true, PK>), dim3((unsigned)((items + 7) / 8 * 8)), dim3(NT), 0, st, \
@@ -738,6 +765,14 @@ void launch_dense_swiglu(int64_t T, int d, int I, bool packed, const void* x, co
 
 void launch_dense_down(int64_t T, int d, int I, bool packed, const void* h, const void* Wd, float* y, hipStream_t st) {
     const int n_nb = (d + GN - 1) / GN;
+    const uint64_t h_bytes = (uint64_t)T * I * 2;
+    if (packed && I % (WK * WUN) == 0 && h_bytes < ((uint64_t)1 << 32)) {
+        const int ws_items = (int)((T + GM - 1) / GM) * n_nb;
+        hipLaunchKernelGGL((grouped_gemm_ws_kernel<1, true>), dim3((unsigned)((ws_items + 7) / 8 * 8)),
+                           dim3(64 * WNW), 0, st, (const u16*)h, (uint32_t)h_bytes, nullptr, nullptr, nullptr,
+                           nullptr, (const u16*)Wd, nullptr, 1, y, I, d, n_nb, GM, (int)T);
+        return;
+    }
     const int items = (int)((T + GM - 1) / GM) * n_nb;
 #define BEAM_DDN(PK)                                                                                          \
     hipLaunchKernelGGL((grouped_gemm_kernel<1, true, PK>), dim3((unsigned)((items + 7) / 8 * 8)), dim3(NT), 0, st, \
