@@ -73,7 +73,8 @@ def test_dense_beam_shape_sampled(cfg):
 
 
 def test_dense_smallest_intermediate_every_token():
-    """The smallest accepted intermediate size (I = 2048) at d = 2048 and T = 2000, every token:
+    """The smallest accepted intermediate size (I = 2048) at d = 2048 and T = 2000, every token, with
+    row-major and packed weights:
     where the bf16 rounding of h from FP32 sums weighs most against the output bar (at I = 512 a
     single one-ulp difference of a large h reaches about 1e-2 rms(y), which is why the entry point
     rejects I < 2048)."""
@@ -86,3 +87,7 @@ def test_dense_smallest_intermediate_every_token():
     print("%s: max|dy| %.3e, rms %.3e, ratio %.2e" % (w.name, err, rms, err / rms))
     assert np.isfinite(y).all()
     assert err <= P.Y_TOL * rms
+    # packed weights: the weight-streaming GEMMs (7 m-tiles of 320 tokens x 16 n-blocks for gate/up,
+    # 8 of 256 x 8 for down, XCD by XCD), bitwise equal to the LDS-staged ones on every token
+    yp = _run(w, t, moe.pack_dense_weights(t["Wg"], t["Wu"], t["Wd"]))
+    assert np.array_equal(y.view(np.uint32), yp.view(np.uint32))
