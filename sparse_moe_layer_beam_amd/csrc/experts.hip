@@ -1,6 +1,6 @@
 // Routed experts of the Beam MoE layer: grouped SwiGLU (gate/up) GEMM with the
-// activation fused, grouped down-projection GEMM with the routing weight fused, and a
-// deterministic combine. BF16 MFMA with FP32 accumulation; silu(g)*u in FP32; h is
+// activation fused, grouped down-projection GEMM (unweighted rows), and a deterministic
+// combine that applies the routing weights. BF16 MFMA with FP32 accumulation; silu(g)*u in FP32; h is
 // rounded to bf16 once, for the bf16 down GEMM.
 //
 // Method: Transformers "Beam" model page (Overview: sparse MoE item, FP32 SwiGLU note;

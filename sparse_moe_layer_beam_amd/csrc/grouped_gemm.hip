@@ -6,9 +6,12 @@
 // BeamConfig: moe_intermediate_size, hidden_act) and archdb "Beam-1.0-501B-A23B" fact
 // sheet (FFN rows: SwiGLU without biases).
 //
-// Tile: up to 256 tokens of one expert x 256 weight rows (gate/up: 128 gate channels and
-// the same 128 up channels; down: 256 output channels), k in stages of 64. Eight waves, two
-// per SIMD, each a 128-token x 64-row register tile (128 FP32 accumulators per lane).
+// Two kernels: grouped_gemm_kernel (below; row-major weights, and shapes the second does not
+// take) stages both operands through LDS; grouped_gemm_ws_kernel (further below; packed weights)
+// streams the weights into registers. The first one's tile: up to 256 tokens of one expert x
+// 256 weight rows (gate/up: 128 gate channels and the same 128 up channels; down: 256 output
+// channels), k in stages of 64. Eight waves, two per SIMD, each a 128-token x 64-row register
+// tile (128 FP32 accumulators per lane).
 //
 // Why this shape on gfx950:
 //  * Both operands reach LDS through direct-to-LDS loads (global_load_lds_dwordx4): no
