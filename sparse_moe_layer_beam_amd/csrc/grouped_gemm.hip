@@ -406,7 +406,15 @@ constexpr int WNW = 8;                    // waves per block
 constexpr int WTB = WM * WK;              // bf16 of one token buffer (40 KB)
 constexpr int WNB = 4;                    // token buffers
 constexpr int WDT = WNB - 1;              // token stages loaded ahead
-constexpr int WPF = 4;                    // token fragments read from LDS ahead of their MFMAs
+// Token fragments read from LDS ahead of their MFMAs: four, but two in the down GEMM's 20-subtile
+// tiles. With four there the allocator spilled 6 VGPRs, and each reload inside the k loop waited
+// for vmcnt(0): every token and weight load in flight, twice per eight stages. With two the
+// kernel has no scratch. On MI355X: down 2.12 -> 2.07-2.08 ms at T=8192, 6.59 -> 6.42 ms at
+// T=32768, bitwise the same (only the read-ahead changes).
+template <int MODE, int LH>
+constexpr int ws_pf() {
+    return MODE == 1 && LH >= 20 ? 2 : 4;
+}
 constexpr int WUN = 8;                    // stages per loop iteration (divides the stage count)
 constexpr int kRsrcWord3 = 0x00020000;    // raw buffer, 32-bit data format (gfx9 V# word 3)
 
@@ -506,6 +514,7 @@ __device__ __forceinline__ void ws_run(u16* lds, __amdgpu_buffer_rsrc_t trs, con
             tload(s + WDT);
             ws_fence();
             const u16* const tb = lds + (s % WNB) * WTB;
+            constexpr int WPF = ws_pf<MODE, LH>();
             bf16x8 xr[WPF];
 #pragma unroll
             for (int f = 0; f < WPF; ++f)
