@@ -36,6 +36,8 @@
 // Packed weights whose k runs are multiples of 512 take a second kernel instead
 // (grouped_gemm_ws_kernel, below): the same items and arithmetic, weights streamed from
 // memory straight into registers and only the tokens staged in LDS.
+#include <atomic>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -400,6 +402,16 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(
 //    of fragment reads per full stage, which LDS serves at about 200 bytes per clock.
 //  * every load is a buffer load (a per-lane offset fixed for the item, the stage in a scalar
 //    offset) and runs on every path, so the compiler counts its own waits on the ring precisely.
+//  * the grouped launches are persistent: one block per CU walks its XCD's items. The next item
+//    is claimed one loop iteration before the current one ends (an atomic whose result is read
+//    only after the k loop), and the next item starts right after the current item's epilogue
+//    stores are issued, with no block launch and no claim latency in between. On MI355X, against
+//    one block per item (same box, alternating builds, results bitwise the same): T=8192 layer
+//    6.01 -> 5.89 ms (gate/up 3.52-3.55 -> 3.39-3.46 ms), T=4096 skewed 3.85-3.99 -> 3.80-3.82,
+//    T=32768 18.73-18.80 -> 18.51-18.67. Issuing the next item's token loads before the stores
+//    (so that the stores drain under its first stages) measured 13% slower for gate/up: with the
+//    prologue's loads out of the steady state's order the compiler's waits on the weight ring
+//    tighten in every stage.
 constexpr int WM = 320;                   // tokens per tile at most
 constexpr int WK = 64;                    // k per stage
 constexpr int WNW = 8;                    // waves per block
@@ -432,6 +444,67 @@ __device__ __forceinline__ void ws_fence() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// Claim state of a persistent launch: the per-XCD counters, this block's XCD and the item split.
+struct ClaimQ {
+    int32_t* q;
+    int x, per_xcd, n_items;
+};
+
+// One claim from the block's own XCD range, issued ahead: the counter's old value. The caller
+// reads it only after the k loop (claim_next), so no wait for it lands inside the loop. The
+// address goes through a VGPR: for a uniform address the compiler would reduce the atomic over
+// the wave and broadcast its result at once, waiting for it (and every load before it) there.
+__device__ __forceinline__ int claim_own_raw(const ClaimQ& c) {
+    int z = 0;
+    asm volatile("" : "+v"(z));
+    return atomicAdd(c.q + c.x + z, 1);
+}
+
+// The item that claim's counter value names, or -2 if the range was spent (for good).
+__device__ __forceinline__ int claim_own_item(const ClaimQ& c, int v) {
+    const int len = min(c.per_xcd, c.n_items - c.x * c.per_xcd);
+    return v < len ? c.x * c.per_xcd + v : -2;
+}
+
+// After an item: lane 0 of wave 0 holds the claim made ahead (claim_own_raw); a spent range sends it
+// to the other XCDs' ranges as in claim_item. The item reaches every wave through the first LDS
+// word: the waves have finished reading the token buffers (first barrier) and read the word
+// before any wave loads into LDS again (last barrier). The barriers wait for LDS work only, so
+// the epilogue stores issued before them keep draining.
+__device__ __forceinline__ int claim_next(const ClaimQ& c, int ahead, u16* lds) {
+    int32_t* const word = reinterpret_cast<int32_t*>(lds);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (threadIdx.x == 0) {
+        int got = claim_own_item(c, ahead);
+        if (got == -2) {
+            got = -1;
+            for (int tries = 0; tries < 16; ++tries) {
+                int most = 0, y = -1;
+                for (int z = 0; z < 8; ++z) {
+                    const int left = min(c.per_xcd, c.n_items - z * c.per_xcd) -
+                                     __hip_atomic_load(c.q + z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if (left > most) {
+                        most = left;
+                        y = z;
+                    }
+                }
+                if (y < 0) break;
+                const int len = min(c.per_xcd, c.n_items - y * c.per_xcd);
+                const int v = atomicAdd(c.q + y, 1);
+                if (v < len) {
+                    got = y * c.per_xcd + v;
+                    break;
+                }
+            }
+        }
+        *reinterpret_cast<volatile int32_t*>(word) = got;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    const int item = __builtin_amdgcn_readfirstlane(*reinterpret_cast<volatile int32_t*>(word));
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    return item;
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t ws_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
 }
@@ -455,7 +528,7 @@ template <int MODE, int LH, int NTT>
 __device__ __forceinline__ void ws_run(u16* lds, __amdgpu_buffer_rsrc_t trs, const uint32_t (&toff)[NTT],
                                        const __amdgpu_buffer_rsrc_t (&wrs)[2], int nstages, int wave, int lane,
                                        int rows, size_t orow0, const int (&chq)[2], int Ndim,
-                                       void* __restrict__ out) {
+                                       void* __restrict__ out, const ClaimQ& cq, int& next) {
     constexpr int NT = ws_nt<LH>();           // token loads per stage
     static_assert(NTT == NT, "one token offset per token load");
     constexpr int NWL = 4;                    // weight loads per stage: 2 blocks x 2 k-halves
@@ -506,6 +579,9 @@ __device__ __forceinline__ void ws_run(u16* lds, __amdgpu_buffer_rsrc_t trs, con
     // fewer loads follow stage 0's tokens here than in the steady state: wait for them now
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(WAIT0) : "memory");
     for (int s0 = 0; s0 < nstages; s0 += WUN) {
+        // the next item's first claim, one loop iteration (WUN stages) before this item ends; an
+        // extra load in flight only makes the counted waits below wait for more, never less
+        if (cq.q && s0 + WUN >= nstages && threadIdx.x == 0) next = claim_own_raw(cq);
 #pragma unroll
         for (int r = 0; r < WUN; ++r) {
             const int s = s0 + r;
@@ -573,7 +649,8 @@ template <int MODE, int LH>
 __device__ __forceinline__ void ws_item(u16* lds, const u16* __restrict__ act, uint32_t act_bytes,
                                         const int32_t* __restrict__ sorted_pairs, int top_k, int beg, int m0, int rows,
                                         int e, int n0, const u16* W0, const u16* W1,
-                                        void* __restrict__ out, int Kdim, int Ndim, int wave, int lane) {
+                                        void* __restrict__ out, int Kdim, int Ndim, int wave, int lane,
+                                        const ClaimQ& cq, int& next) {
     // token offsets: load i of this wave covers rows 8(8i + wave) .. +8 of the tile, lane row
     // + lane/8, global chunk (lane % 8) ^ (lane / 8); rows past the expert's segment repeat its last
     constexpr int NT = ws_nt<LH>();
@@ -608,7 +685,7 @@ __device__ __forceinline__ void ws_item(u16* lds, const u16* __restrict__ act, u
         const size_t blk = ((size_t)e * Ndim + min(ch, Ndim - 16)) / 16;
         wrs[q] = ws_rsrc(W + blk * (size_t)Kdim * 16, (uint32_t)Kdim * 32u);
     }
-    ws_run<MODE, LH>(lds, trs, toff, wrs, Kdim / WK, wave, lane, rows, (size_t)(beg + m0), chq, Ndim, out);
+    ws_run<MODE, LH>(lds, trs, toff, wrs, Kdim / WK, wave, lane, rows, (size_t)(beg + m0), chq, Ndim, out, cq, next);
 }
 
 // MODE 0: out = h [P, I] bf16 = bf16(silu(act . Wg^T) * (act . Wu^T)), act = x rows gathered
@@ -627,57 +704,65 @@ __global__ __launch_bounds__(64 * WNW, 1) void grouped_gemm_ws_kernel(
         const u16* W0, const u16* W1, int top_k, void* __restrict__ out, int Kdim,
         int Ndim, int n_nb, int tile_m, int act_rows) {
     __shared__ __attribute__((aligned(1024))) u16 lds[WNB * WTB];
-    int e, beg, n_e, cnt, local;
+    // one work item: an expert's m-tile x n-block (see below)
+    auto run_item = [&](int e, int beg, int n_e, int cnt, int local, const ClaimQ& cq, int& next) {
+        // the expert's n_nb x cnt items in groups of four n-blocks, m-tile-major inside a group (on
+        // MI355X, against groups of two: T=8192 layer 6.32 -> 6.15 ms, T=32768 19.9 -> 19.75; eight: 6.26)
+        constexpr int GW = 4;
+        const int grp = local / (GW * cnt);
+        const int gw = min(GW, n_nb - grp * GW);
+        const int in = local - grp * GW * cnt;
+        const int mt = in / gw;
+        const int nb = grp * GW + (in - mt * gw);
+        const int m0 = mt * tile_m;
+        const int rows = min(tile_m, n_e - m0);
+        const int n0 = nb * (MODE == 0 ? 128 : 256);
+        // opaque per item, so that the compiler does not hoist the lane-derived addresses of all
+        // ten tile forms out of the item loop (they would stay live across it and spill)
+        int lane = threadIdx.x & 63;
+        asm volatile("" : "+v"(lane));
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        // live 16-token subtiles, in pairs
+        const int lh = min(WM / 16, 2 * ((rows + 31) / 32));
+        switch (lh) {
+#define BEAM_WS_CASE(L)                                                                                         \
+    case L:                                                                                                     \
+        ws_item<MODE, L>(lds, act, act_bytes, sorted_pairs, top_k, beg, m0, rows, e, n0, W0, W1, out,          \
+                         Kdim, Ndim, wave, lane, cq, next);                                                     \
+        break;
+            BEAM_WS_CASE(2) BEAM_WS_CASE(4) BEAM_WS_CASE(6) BEAM_WS_CASE(8)
+            BEAM_WS_CASE(10) BEAM_WS_CASE(12) BEAM_WS_CASE(14) BEAM_WS_CASE(16) BEAM_WS_CASE(18) BEAM_WS_CASE(20)
+#undef BEAM_WS_CASE
+        }
+    };
     if constexpr (DENSE) {
         const int n_mt = (act_rows + tile_m - 1) / tile_m;
         const int n_items = n_mt * n_nb;
         const int per_xcd = (n_items + 7) / 8;
         const int slot = blockIdx.x >> 3;
         if (slot >= per_xcd) return;
-        local = (blockIdx.x & 7) * per_xcd + slot;
+        const int local = (blockIdx.x & 7) * per_xcd + slot;
         if (local >= n_items) return;
-        e = 0;
-        beg = 0;
-        n_e = act_rows;
-        cnt = n_mt;
+        const ClaimQ none{nullptr, 0, 0, 0};
+        int unused = -1;
+        run_item(0, 0, act_rows, n_mt, local, none, unused);
     } else {
+        // persistent: one block per CU walks items until every item is claimed; the claim of the
+        // next item is made before the current one ends, and each item's epilogue stores drain
+        // while the next item's loads start
         const int n_items = *n_tiles_p * n_nb;
-        const int per_xcd = (n_items + 7) / 8;
-        if ((int)blockIdx.x >= n_items + n_items / 4 + 64) return;
-        const int item = claim_item(n_tiles_p + 1 + 8 * MODE, blockIdx.x & 7, per_xcd, n_items, lds);
-        if (item < 0) return;
-        const int j = item / n_nb;
-        e = tiles[4 * j];
-        const int first = tiles[4 * j + 2];
-        cnt = tiles[4 * j + 3];
-        local = item - first * n_nb;
-        beg = offsets[e];
-        n_e = offsets[e + 1] - beg;
-    }
-    // the expert's n_nb x cnt items in groups of four n-blocks, m-tile-major inside a group (on
-    // MI355X, against groups of two: T=8192 layer 6.32 -> 6.15 ms, T=32768 19.9 -> 19.75; eight: 6.26)
-    constexpr int GW = 4;
-    const int grp = local / (GW * cnt);
-    const int gw = min(GW, n_nb - grp * GW);
-    const int in = local - grp * GW * cnt;
-    const int mt = in / gw;
-    const int nb = grp * GW + (in - mt * gw);
-    const int m0 = mt * tile_m;
-    const int rows = min(tile_m, n_e - m0);
-    const int n0 = nb * (MODE == 0 ? 128 : 256);
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    // live 16-token subtiles, in pairs
-    const int lh = min(WM / 16, 2 * ((rows + 31) / 32));
-    switch (lh) {
-#define BEAM_WS_CASE(L)                                                                                         \
-    case L:                                                                                                     \
-        ws_item<MODE, L>(lds, act, act_bytes, sorted_pairs, top_k, beg, m0, rows, e, n0, W0, W1, out,          \
-                         Kdim, Ndim, wave, lane);                                                               \
-        break;
-        BEAM_WS_CASE(2) BEAM_WS_CASE(4) BEAM_WS_CASE(6) BEAM_WS_CASE(8)
-        BEAM_WS_CASE(10) BEAM_WS_CASE(12) BEAM_WS_CASE(14) BEAM_WS_CASE(16) BEAM_WS_CASE(18) BEAM_WS_CASE(20)
-#undef BEAM_WS_CASE
+        const ClaimQ cq{n_tiles_p + 1 + 8 * MODE, (int)(blockIdx.x & 7), (n_items + 7) / 8, n_items};
+        int item = claim_item(cq.q, cq.x, cq.per_xcd, n_items, lds);
+        while (item >= 0) {
+            const int j = item / n_nb;
+            const int e = tiles[4 * j];
+            const int first = tiles[4 * j + 2];
+            const int cnt = tiles[4 * j + 3];
+            const int beg = offsets[e];
+            int next = 0x7fffffff;    // the claim made ahead: a counter value (none: spent)
+            run_item(e, beg, offsets[e + 1] - beg, cnt, item - first * n_nb, cq, next);
+            item = claim_next(cq, next, lds);
+        }
     }
 }
 
@@ -685,6 +770,21 @@ __global__ __launch_bounds__(64 * WNW, 1) void grouped_gemm_ws_kernel(
 // activations that 32-bit buffer offsets reach.
 bool ws_supports(const Shape& s, int Kdim, uint64_t act_bytes) {
     return s.packed && Kdim % (WK * WUN) == 0 && act_bytes < ((uint64_t)1 << 32);
+}
+
+// Blocks of a persistent weight-streaming launch: one per CU of the current device (a multiple of
+// the 8 XCDs, so that every XCD's range has its share of blocks), looked up once per device.
+int ws_grid() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    int cus = cached[dev].load(std::memory_order_relaxed);
+    if (cus == 0) {
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8) cus = 256;
+        cus = cus / 8 * 8;
+        cached[dev].store(cus, std::memory_order_relaxed);
+    }
+    return cus;
 }
 
 int max_items(const Shape& s, int n_nb, int tile_m) {
@@ -719,7 +819,8 @@ void launch_gemm_swiglu(const Shape& s, const void* x, const int32_t* offsets, c
     const int blocks = (max_items(s, n_nb, tile_m) + 7) / 8 * 8;
     const uint64_t x_bytes = (uint64_t)s.T * s.d * 2;
     if (ws_supports(s, s.d, x_bytes)) {
-        hipLaunchKernelGGL((grouped_gemm_ws_kernel<0, false>), dim3((unsigned)blocks), dim3(64 * WNW), 0, st,
+        hipLaunchKernelGGL((grouped_gemm_ws_kernel<0, false>), dim3((unsigned)std::min(blocks, ws_grid())),
+                           dim3(64 * WNW), 0, st,
                            (const u16*)x, (uint32_t)x_bytes, offsets, sorted_pairs, tiles, n_tiles, (const u16*)Wg,
                            (const u16*)Wu, s.K, h, s.d, s.I, n_nb, tile_m, 0);
         return;
@@ -740,7 +841,8 @@ void launch_gemm_down(const Shape& s, const void* h, const int32_t* offsets, con
     const int blocks = (max_items(s, n_nb, tile_m) + 7) / 8 * 8;
     const uint64_t h_bytes = (uint64_t)s.T * s.K * s.I * 2;
     if (ws_supports(s, s.I, h_bytes)) {
-        hipLaunchKernelGGL((grouped_gemm_ws_kernel<1, false>), dim3((unsigned)blocks), dim3(64 * WNW), 0, st,
+        hipLaunchKernelGGL((grouped_gemm_ws_kernel<1, false>), dim3((unsigned)std::min(blocks, ws_grid())),
+                           dim3(64 * WNW), 0, st,
                            (const u16*)h, (uint32_t)h_bytes, offsets, sorted_pairs, tiles, n_tiles, (const u16*)Wd,
                            nullptr, s.K, y_perm, s.I, s.d, n_nb, tile_m, 0);
         return;
