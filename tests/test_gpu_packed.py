@@ -121,8 +121,15 @@ def test_forward_packed_against_oracle_mid():
 # stays on the LDS-staged GEMM
 # ws_mid_T1500: both expert GEMMs on the weight-streaming kernel, tiles of 320 tokens whose live
 # 16-token subtile counts (oracle routing) take every value 2, 4, .., 20; ws_d384_T800: gate/up on
-# the LDS-staged kernel (d not a multiple of 512), down weight-streaming on tiles of 256
+# the LDS-staged kernel (d not a multiple of 512), down weight-streaming on tiles of 256.
+# The weight-streaming launches are persistent (one block per CU walks its XCD's range of items):
+# ws_e2_T40 has fewer items than XCDs (gate/up 8, down 4: XCD ranges of one item or none);
+# ws_mid_T4000 gives each block several items of different tile heights, and the blocks whose
+# XCD range runs out first take items from the other ranges.
 WS_CASES = {
+    "ws_e2_T40": recipes.Workload(44, "ws_e2_T40", T=40, d=512, E=2, n_group=1, topk_group=1, top_k=1, I=512),
+    "ws_mid_T4000": recipes.Workload(45, "ws_mid_T4000", T=4000, d=512, E=64, n_group=8, topk_group=4, top_k=8,
+                                     I=512),
     "ws_mid_T1500": recipes.Workload(42, "ws_mid_T1500", T=1500, d=512, E=64, n_group=8, topk_group=4, top_k=8,
                                      I=512, hot_experts=4, hot_bias=0.5),
     "ws_d384_T800": recipes.Workload(43, "ws_d384_T800", T=800, d=384, E=32, n_group=4, topk_group=2, top_k=4,
