@@ -466,16 +466,20 @@ __device__ __forceinline__ int claim_own_item(const ClaimQ& c, int v) {
     return v < len ? c.x * c.per_xcd + v : -2;
 }
 
-// After an item: lane 0 of wave 0 holds the claim made ahead (claim_own_raw); a spent range sends it
-// to the other XCDs' ranges as in claim_item. The item reaches every wave through the first LDS
-// word: the waves have finished reading the token buffers (first barrier) and read the word
-// before any wave loads into LDS again (last barrier). The barriers wait for LDS work only, so
-// the epilogue stores issued before them keep draining.
-__device__ __forceinline__ int claim_next(const ClaimQ& c, int ahead, u16* lds) {
-    int32_t* const word = reinterpret_cast<int32_t*>(lds);
+typedef __attribute__((address_space(3))) int32_t lds_i32;
+
+// After an item: lane 0 of wave 0 holds the item claimed ahead (claim_own_item of claim_own_raw's
+// value, resolved before the epilogue stores are issued); a spent range (-2) sends it to the other
+// XCDs' ranges as in claim_item. The item reaches every wave through the first LDS word: the waves
+// have finished reading the token buffers (first barrier) and read the word before any wave loads
+// into LDS again (last barrier). The word is accessed through an LDS pointer (ds instructions,
+// counted by lgkmcnt) and the barriers wait for LDS work only, so the epilogue stores issued before
+// them keep draining: a volatile access through a generic pointer compiles to a flat access, and
+// the wait for it (vmcnt(0)) would wait for every store.
+__device__ __forceinline__ int claim_next(const ClaimQ& c, int got, u16* lds) {
+    lds_i32* const word = (lds_i32*)(lds);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if (threadIdx.x == 0) {
-        int got = claim_own_item(c, ahead);
         if (got == -2) {
             got = -1;
             for (int tries = 0; tries < 16; ++tries) {
@@ -497,10 +501,10 @@ __device__ __forceinline__ int claim_next(const ClaimQ& c, int ahead, u16* lds) 
                 }
             }
         }
-        *reinterpret_cast<volatile int32_t*>(word) = got;
+        *word = got;
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    const int item = __builtin_amdgcn_readfirstlane(*reinterpret_cast<volatile int32_t*>(word));
+    const int item = __builtin_amdgcn_readfirstlane(*word);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     return item;
 }
@@ -614,6 +618,8 @@ __device__ __forceinline__ void ws_run(u16* lds, __amdgpu_buffer_rsrc_t trs, con
     }
     // the last (clamped, unused) loads must land before the block's LDS is released
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // the claim made ahead has returned too: read it now, before any store is in flight
+    if (cq.q && threadIdx.x == 0) next = claim_own_item(cq, next);
 
     // Epilogue. acc[i][q][v]: token 16*i + lane%16 of the tile, channel chq[q] + 4*(lane/16) + v
     // (gate/up: q = 0 gate and q = 1 up of the same channels).
