@@ -200,7 +200,10 @@ __device__ __forceinline__ void gemm_run(u16* lds, const u16* const (&src)[DMA],
 // are needed. Lane 0 of wave 0 claims; the result reaches the other waves through the first
 // LDS word, before any load into LDS is issued.
 __device__ __forceinline__ int claim_item(int32_t* q, int x, int per_xcd, int n_items, u16* lds) {
-    int32_t* const word = reinterpret_cast<int32_t*>(lds);
+    // an LDS-typed pointer: ds instructions (a volatile access through a generic pointer would be a
+    // flat one, whose wait also counts every global load and store in flight)
+    __attribute__((address_space(3))) volatile int32_t* const word =
+        (__attribute__((address_space(3))) volatile int32_t*)(lds);
     if (threadIdx.x == 0) {
         int got = -1, y = x;
         for (int tries = 0; tries < 16; ++tries) {
@@ -227,7 +230,7 @@ __device__ __forceinline__ int claim_item(int32_t* q, int x, int per_xcd, int n_
         *word = got;
     }
     __syncthreads();
-    const int item = __builtin_amdgcn_readfirstlane(*reinterpret_cast<volatile int32_t*>(word));
+    const int item = __builtin_amdgcn_readfirstlane(*word);
     __syncthreads();
     return item;
 }
