@@ -11,6 +11,7 @@ import synth
 import sparse_moe_layer_beam_amd as moe
 from synth import recipes
 from tests.test_gpu_parity import SMALL
+from tests.test_gpu_packed import WS_CASES
 
 pytestmark = pytest.mark.gpu
 
@@ -36,9 +37,12 @@ def _setup(w, layout):
     return t, args, y
 
 
-@pytest.mark.parametrize("name,layout", [("beam1", 1), ("mid_T2000", 0), ("mid_T2100", 1), ("mid_prenorm_T333", 1)])
+# mid_T2100 (packed): the gate/up GEMM on the persistent weight-streaming kernel; ws_mid_T1500
+# (packed, d = I = 512): both expert GEMMs on it, their work-item counters cleared inside the graph
+@pytest.mark.parametrize("name,layout", [("beam1", 1), ("mid_T2000", 0), ("mid_T2100", 1), ("mid_prenorm_T333", 1),
+                                         ("ws_mid_T1500", 1)])
 def test_graph_replay_matches_eager(name, layout):
-    w = recipes.WORKLOADS[1] if name == "beam1" else SMALL[name]
+    w = recipes.WORKLOADS[1] if name == "beam1" else (WS_CASES[name] if name in WS_CASES else SMALL[name])
     print("case graph", name, layout, flush=True)
     t, args, y = _setup(w, layout)
     moe.beam_moe_forward(*args)
